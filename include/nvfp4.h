@@ -1,0 +1,199 @@
+/*
+ * nvfp4.h -- C ABI of the NVFP4 hot path on AMD Instinct MI355X (gfx950).
+ *
+ * NVFP4 (techwalker.com LongLive-2.0 report summary, section 一): 4-bit E2M1
+ * values; every 16 consecutive values along a row share one FP8 (E4M3) block
+ * scale; the whole tensor shares one FP32 scale.  Weights, activations and
+ * the KV cache all use it, and the linear layers multiply in 4 bits
+ * (zuobiaodaohang LongLive blog, section "NVFP4：数据体积砍到 1/4"; techwalker
+ * summary, section 四).
+ *
+ * Numerics (every rounding is one round-to-nearest-even of the exact value):
+ *   amax    = max |x| over the tensor
+ *   s_g     = RN_fp32(amax / 2688)            (2688 = 6 * 448; s_g = 1 if amax == 0)
+ *   s_b     = RN_e4m3(b / (6 s_g)), saturating at 448, b = max |x| over the block
+ *   code    = sign(x) | RN_e2m1(|x| / (s_b s_g)), saturating at 6; 0 magnitude if s_b == 0
+ *   x^      = q * s_b * s_g
+ * E2M1: sign bit 3, exponent bits 2:1 (bias 1), mantissa bit 0; magnitudes
+ * 0, .5, 1, 1.5, 2, 3, 4, 6.  E4M3: OCP E4M3FN (bias 7, max 448).
+ *
+ * Byte layouts (part of the contract):
+ *   codes   [rows][cols/2] bytes; byte j holds code 2j in bits 3:0 and
+ *           code 2j+1 in bits 7:4.
+ *   scales  NVFP4_SCALES_ROWMAJOR: [rows][cols/16] bytes.
+ *           NVFP4_SCALES_TILED: byte of (row r, block kb) at
+ *             ((r/128) * (cols/64) + kb/4) * 512 + (r%128) * 4 + kb%4
+ *           (rows % 128 == 0 and cols % 64 == 0 required).
+ *
+ * Conventions of every call:
+ *   - All pointers are device pointers unless marked (host).  The caller
+ *     owns every buffer; the library allocates nothing and keeps no state.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and never synchronise the host.  Outputs are valid once the
+ *     stream has reached the call.
+ *   - Return value: NVFP4_OK or a negative nvfp4_status_t.  Arguments are
+ *     checked before anything is launched; on an error nothing is launched
+ *     and no output is touched, except NVFP4_EHIP (a launch failed).
+ *   - Quantized buffers are opaque bytes: never cast them to another dtype
+ *     (LongLive 2.0 README copy on news.ainew.jp, section "NVFP4": a dtype
+ *     cast of the quantized buffers corrupts them).
+ *   - Non-finite inputs and amax < 2688 * 2^-126 are outside the contract:
+ *     the outputs are unspecified, but no call reads or writes out of bounds.
+ *   - Thread safety: there is no mutable library state; concurrent calls
+ *     on different streams are safe when their buffers do not overlap.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_EINVAL = -1,      /* null pointer, bad enum, negative size            */
+  NVFP4_ESHAPE = -2,      /* cols % 16, alignment, layout divisibility, ranges */
+  NVFP4_EWORKSPACE = -3,  /* workspace missing or smaller than required       */
+  NVFP4_EHIP = -4         /* a HIP launch failed (hipGetLastError)            */
+} nvfp4_status_t;
+
+typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype_t;
+
+typedef enum { NVFP4_SCALES_ROWMAJOR = 0, NVFP4_SCALES_TILED = 1 } nvfp4_scale_layout_t;
+
+/* An NVFP4 tensor [rows x cols] (cols % 16 == 0).  The struct itself is a
+ * host object; its pointers are device pointers. */
+typedef struct {
+  uint8_t* codes;        /* rows * cols / 2 bytes                               */
+  uint8_t* scales;       /* rows * cols / 16 bytes, in `scale_layout`           */
+  float* global_scale;   /* one float: s_g                                      */
+  int64_t rows;
+  int64_t cols;
+  int32_t scale_layout;  /* nvfp4_scale_layout_t                                */
+} nvfp4_tensor_t;
+
+/* Operation ids for nvfp4_workspace_bytes. */
+typedef enum { NVFP4_OP_QUANTIZE = 0, NVFP4_OP_KV_QUANTIZE = 1 } nvfp4_op_t;
+
+/* Workspace (device bytes) a call needs.
+ *   NVFP4_OP_QUANTIZE:     a = rows, b = cols, c = 1 if the caller passes amax, else 0
+ *   NVFP4_OP_KV_QUANTIZE:  a = T (tokens), b = n_heads, c = head_dim
+ * Returns 0 for a bad op id.  The workspace must be 256-byte aligned. */
+size_t nvfp4_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c);
+
+/* Quantize X [rows x cols] (fp32 or bf16, row stride ld_x elements) to NVFP4
+ * (techwalker summary, section 一: two-level scaling; the scale and the
+ * quantization are one fused pass per block).
+ *   x          rows x cols input, dtype x_dtype; 16-byte aligned, ld_x * elem % 16 == 0
+ *   amax       NULL: the call computes max|x| (two reads of X);
+ *              else a device float that already holds max|x| (e.g. from
+ *              nvfp4_gemm_w4a4's y_amax) and X is read once.
+ *   out        (host struct) destination: codes, scales in out->scale_layout,
+ *              *out->global_scale = s_g.  out->rows/cols must equal rows/cols.
+ *   workspace  nvfp4_workspace_bytes(NVFP4_OP_QUANTIZE, rows, cols, amax != NULL)
+ * rows == 0 is a no-op (s_g is still written: 1.0).
+ * Errors: EINVAL (nulls, dtype), ESHAPE (cols % 16, alignment, tiled layout
+ * with rows % 128 or cols % 64, ld_x < cols), EWORKSPACE. */
+int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                   const float* amax, const nvfp4_tensor_t* out, void* workspace,
+                   size_t ws_bytes, void* stream);
+
+/* Dequantize: y = RN(q * s_b * s_g) in y_dtype (fp32, or bf16 with one
+ * rounding of the exact product).  y: rows x cols, row stride ld_y elements,
+ * 16-byte aligned with ld_y * elem % 16 == 0.  Parallel dequantization is the
+ * read side of the NVFP4 format (techwalker summary, section 四).
+ * Errors: EINVAL, ESHAPE. */
+int nvfp4_dequantize(const nvfp4_tensor_t* in, void* y, int32_t y_dtype, int64_t ld_y,
+                     void* stream);
+
+/* W4A4 GEMM: Y[M x N] = X[M x K] * W[N x K]^T with both operands NVFP4
+ * (techwalker summary, section 四: every matrix multiplication in 4 bits).
+ * Y = s_gx * s_gw * sum_k (q_x s_bx)(q_w s_bw): the block products are exact
+ * and accumulate in fp32; the result is stored as y_dtype (fp32 or bf16, RNE).
+ *   x, w    (host structs) K = x->cols = w->cols, K % 64 == 0; any scale layout
+ *   y       M x N, row stride ld_y elements (ld_y >= N), 4-byte aligned rows
+ *   y_amax  NULL, or a device float that the call max-folds max|Y as stored|
+ *           into (atomic max; initialise it to 0 before the first GEMM whose
+ *           amax it should hold).  Lets the next quantize read Y once.
+ * M == 0 or N == 0 is a no-op.
+ * Errors: EINVAL, ESHAPE (K mismatch, K % 64, ld_y). */
+int nvfp4_gemm_w4a4(const nvfp4_tensor_t* x, const nvfp4_tensor_t* w, void* y, int32_t y_dtype,
+                    int64_t ld_y, float* y_amax, void* stream);
+
+/* Paged NVFP4 KV cache (techwalker summary, section 四, second key: K gets a
+ * simple mean subtraction, then K and V are stored in NVFP4; the cache is
+ * read as many blocks of a window at once; zuobiaodaohang blog: the quantized
+ * cache is updated in place).
+ *
+ * Page byte layout (page_bytes = 2 * n_heads * page_tokens * head_dim * 9/16):
+ *   K codes  [n_heads][page_tokens][head_dim/2]
+ *   K scales [n_heads][page_tokens][head_dim/16]   (E4M3, blocks of 16 along head_dim)
+ *   V codes  [n_heads][page_tokens][head_dim/2]
+ *   V scales [n_heads][page_tokens][head_dim/16]
+ * Token position p of a layer lives in logical page p / page_tokens, slot
+ * p % page_tokens, physical page page_table[layer][p / page_tokens].
+ * Each written chunk c of a layer has its own K mean mu[h][d] (fp32) and
+ * global scales s_gK, s_gV.  page_chunk[layer][lp] = {c_first, split}: slots
+ * [0, split) belong to chunk c_first, slots [split, page_tokens) to c_first+1. */
+typedef struct {
+  uint8_t* pool;              /* n_phys_pages * page_bytes                        */
+  int64_t n_phys_pages;
+  int32_t n_layers;
+  int32_t n_heads;
+  int32_t head_dim;           /* % 16 == 0, <= 256                                */
+  int32_t page_tokens;        /* > 0                                              */
+  int32_t max_pages;          /* logical pages per layer                          */
+  int32_t max_chunks;         /* chunks per layer                                 */
+  const int32_t* page_table;  /* [n_layers][max_pages] -> physical page            */
+  int32_t* page_chunk;        /* [n_layers][max_pages][2], written by kv_quantize  */
+  float* k_mean;              /* [n_layers][max_chunks][n_heads][head_dim]         */
+  float* k_gscale;            /* [n_layers][max_chunks]                            */
+  float* v_gscale;            /* [n_layers][max_chunks]                            */
+} nvfp4_kv_cache_t;
+
+/* Bytes of one page. */
+int64_t nvfp4_kv_page_bytes(int32_t n_heads, int32_t head_dim, int32_t page_tokens);
+
+/* Write chunk `chunk_id` of `layer`: tokens [start_token, start_token + T)
+ * from K, V bf16 [T][n_heads][head_dim] (contiguous, 16-byte aligned).
+ *   mu[h][d] = RN32(exact mean over the T tokens of K[.][h][d]),
+ *   K' = RN32(K - mu), s_gK from max|K'|, s_gV from max|V|,
+ *   K', V quantized along head_dim and stored in place in their pages;
+ *   k_mean / k_gscale / v_gscale / page_chunk updated.
+ * Chunks of a layer are written in order, chunk c + 1 starting where chunk
+ * c ended (so a page holds at most two chunks).  The page table entries for
+ * the touched pages must be valid physical pages.  The mean is accumulated in
+ * fp64 in a fixed order; it is exact while the partial sums of a channel stay
+ * within fp64's 53 bits (true for bf16 data of moderate dynamic range).
+ * Errors: EINVAL, ESHAPE (T < page_tokens unless it is chunk 0, head_dim,
+ * token range past max_pages, chunk_id >= max_chunks), EWORKSPACE. */
+int nvfp4_kv_quantize(const nvfp4_kv_cache_t* cache, int32_t layer, int32_t chunk_id,
+                      const void* k_bf16, const void* v_bf16, int64_t T, int64_t start_token,
+                      void* workspace, size_t ws_bytes, void* stream);
+
+/* Dequantize the pages of a window in one launch (techwalker summary,
+ * section 四: one parallel kernel decompresses many cache blocks of a time
+ * window).  For each listed logical page, in list order:
+ *   K^ = RN_bf16(q s_b s_gK + mu),  V^ = RN_bf16(q s_b s_gV)   (one rounding each)
+ * using the chunk of every slot (page_chunk).
+ *   logical_pages  device int32[n_pages], each in [0, max_pages)
+ *   k_out, v_out   bf16 [n_pages * page_tokens][n_heads][head_dim], 16-byte aligned
+ * Errors: EINVAL, ESHAPE. */
+int nvfp4_kv_dequant_blocks(const nvfp4_kv_cache_t* cache, int32_t layer,
+                            const int32_t* logical_pages, int32_t n_pages, void* k_out,
+                            void* v_out, void* stream);
+
+/* Library version and messages. */
+int nvfp4_abi_version(void);
+const char* nvfp4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -9,6 +9,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+# The HIP library is built in-tree; build it here only if nothing is built yet.
+if not os.path.exists(os.path.join(ROOT, "w4a4_gemm_amd", "libnvfp4.so")):
+    from w4a4_gemm_amd import build as _build
+    _build.build()
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")

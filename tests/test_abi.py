@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every symbol the header declares, and rejects
+bad arguments before launching anything (CPU only: no compute calls)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "nvfp4.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_hot_path_calls():
+    names = _declared_functions()
+    for n in ("nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm_w4a4", "nvfp4_kv_quantize",
+              "nvfp4_kv_dequant_blocks"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import w4a4_gemm_amd as nv
+    lib = ctypes.CDLL(nv.LIB_PATH)
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(nv.EXPORTS) <= set(_declared_functions())
+
+
+def test_version_and_status_strings():
+    import w4a4_gemm_amd as nv
+    assert nv.nvfp4_abi_version() == 1
+    assert nv.nvfp4_status_string(0) == "ok"
+    assert "shape" in nv.nvfp4_status_string(-2)
+    assert nv.nvfp4_status_string(123) == "unknown status"
+
+
+def test_workspace_and_page_sizes():
+    import w4a4_gemm_amd as nv
+    assert nv.nvfp4_kv_page_bytes(24, 128, 256) == 884736
+    assert nv.nvfp4_kv_page_bytes(24, 120, 256) == 0
+    assert nv.nvfp4_workspace_bytes(nv.OP_QUANTIZE, 4096, 3072, 1) == 0
+    assert nv.nvfp4_workspace_bytes(nv.OP_QUANTIZE, 4096, 3072, 0) > 0
+    assert nv.nvfp4_workspace_bytes(nv.OP_KV_QUANTIZE, 7040, 24, 128) > 0
+    assert nv.nvfp4_workspace_bytes(99, 1, 1, 1) == 0
+
+
+def test_argument_errors_return_before_launch():
+    import w4a4_gemm_amd as nv
+    lib = nv._lib
+    T = nv._Tensor
+    good = T(16, 16, 64, 128, 64, nv.SCALES_ROWMAJOR)
+    # bad dtype / null input
+    assert lib.nvfp4_quantize(16, 7, 128, 64, 64, None, ctypes.byref(good), None, 0, None) == nv.EINVAL
+    assert lib.nvfp4_quantize(None, nv.BF16, 128, 64, 64, None, ctypes.byref(good), 256, 4096,
+                              None) == nv.EINVAL
+    # cols % 16
+    bad = T(16, 16, 64, 128, 40, nv.SCALES_ROWMAJOR)
+    assert lib.nvfp4_quantize(16, nv.BF16, 128, 40, 40, None, ctypes.byref(bad), None, 0,
+                              None) == nv.ESHAPE
+    # tiled layout needs rows % 128
+    tiled = T(16, 16, 64, 100, 64, nv.SCALES_TILED)
+    assert lib.nvfp4_quantize(16, nv.BF16, 100, 64, 64, None, ctypes.byref(tiled), None, 0,
+                              None) == nv.ESHAPE
+    # missing workspace
+    assert lib.nvfp4_quantize(16, nv.BF16, 128, 64, 64, None, ctypes.byref(good), None, 0,
+                              None) == nv.EWORKSPACE
+    # ld_x < cols
+    assert lib.nvfp4_quantize(16, nv.BF16, 128, 64, 32, None, ctypes.byref(good), 256, 4096,
+                              None) == nv.ESHAPE
+    # GEMM K mismatch and K % 64
+    w = T(16, 16, 64, 64, 128, nv.SCALES_ROWMAJOR)
+    assert lib.nvfp4_gemm_w4a4(ctypes.byref(good), ctypes.byref(w), 16, nv.BF16, 64, None,
+                               None) == nv.ESHAPE
+    k48 = T(16, 16, 64, 64, 48, nv.SCALES_ROWMAJOR)
+    assert lib.nvfp4_gemm_w4a4(ctypes.byref(k48), ctypes.byref(k48), 16, nv.BF16, 64, None,
+                               None) == nv.ESHAPE
+    assert lib.nvfp4_gemm_w4a4(ctypes.byref(good), ctypes.byref(good), 16, 5, 128, None,
+                               None) == nv.EINVAL
+    # empty GEMM is a no-op
+    e = T(16, 16, 64, 0, 64, nv.SCALES_ROWMAJOR)
+    assert lib.nvfp4_gemm_w4a4(ctypes.byref(e), ctypes.byref(good), None, nv.BF16, 128, None,
+                               None) == nv.OK
+    # dequantize: bad out dtype
+    assert lib.nvfp4_dequantize(ctypes.byref(good), 16, 9, 64, None) == nv.EINVAL
+
+
+def test_kv_argument_errors():
+    import w4a4_gemm_amd as nv
+    lib = nv._lib
+    C = nv._KVCache
+    good = C(256, 28, 1, 24, 128, 256, 28, 2, 16, 16, 16, 16, 16)
+    # null k
+    assert lib.nvfp4_kv_quantize(ctypes.byref(good), 0, 0, None, 16, 7040, 0, 256, 1 << 20,
+                                 None) == nv.EINVAL
+    # layer out of range, chunk out of range, too many tokens for max_pages
+    assert lib.nvfp4_kv_quantize(ctypes.byref(good), 1, 0, 16, 16, 7040, 0, 256, 1 << 20,
+                                 None) == nv.ESHAPE
+    assert lib.nvfp4_kv_quantize(ctypes.byref(good), 0, 2, 16, 16, 7040, 0, 256, 1 << 20,
+                                 None) == nv.ESHAPE
+    assert lib.nvfp4_kv_quantize(ctypes.byref(good), 0, 0, 16, 16, 7200, 0, 256, 1 << 20,
+                                 None) == nv.ESHAPE
+    # a chunk after the first shorter than a page
+    assert lib.nvfp4_kv_quantize(ctypes.byref(good), 0, 1, 16, 16, 100, 256, 256, 1 << 20,
+                                 None) == nv.ESHAPE
+    # workspace too small
+    assert lib.nvfp4_kv_quantize(ctypes.byref(good), 0, 0, 16, 16, 7040, 0, 256, 16,
+                                 None) == nv.EWORKSPACE
+    # head_dim not a multiple of 16
+    bad = C(256, 28, 1, 24, 120, 256, 28, 2, 16, 16, 16, 16, 16)
+    assert lib.nvfp4_kv_dequant_blocks(ctypes.byref(bad), 0, 16, 4, 16, 16, None) == nv.ESHAPE
+    # zero pages is a no-op; negative is an error
+    assert lib.nvfp4_kv_dequant_blocks(ctypes.byref(good), 0, None, 0, None, None, None) == nv.OK
+    assert lib.nvfp4_kv_dequant_blocks(ctypes.byref(good), 0, 16, -1, 16, 16, None) == nv.EINVAL

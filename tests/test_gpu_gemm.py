@@ -1,0 +1,176 @@
+"""GPU parity of nvfp4_gemm_w4a4 against the exact oracle product.
+
+Tolerance (stated for the W4A4 GEMM): fp32 output  |Y - Y_ref| <= 1e-3 * A_ref
+with A_ref = sum_k |x^ w^|; bf16 output within one bf16 ulp of RN_bf16(Y_ref),
+or |Y - Y_ref| <= ulp_bf16(Y)/2 + 1e-3 A_ref for at most 0.1% of the elements
+(the cancellation clause).  The operands fed to the GPU are the oracle's own
+NVFP4 bytes, so the GEMM is checked on identical inputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from helpers import bf16_tensor, dev, f32_tensor, from_oracle, to_oracle
+from oracle import formats as F
+from oracle import nvfp4 as Q
+
+pytestmark = pytest.mark.gpu
+
+import w4a4_gemm_amd as nv  # noqa: E402
+
+
+def _operands_from_f32(x, w):
+    return Q.quantize(x.astype(np.float64)), Q.quantize(w.astype(np.float64))
+
+
+def _run(xq, wq, dtype, layout_x=nv.SCALES_TILED, layout_w=nv.SCALES_TILED, amax=False):
+    xt, wt = from_oracle(xq, layout_x), from_oracle(wq, layout_w)
+    am = torch.zeros(1, dtype=torch.float32, device=dev()) if amax else None
+    y = nv.nvfp4_gemm_w4a4(xt, wt, dtype, y_amax=am)
+    torch.cuda.synchronize()
+    out = y.float().cpu().numpy().astype(np.float64)
+    return (out, float(am.cpu()[0])) if amax else out
+
+
+def test_tiny_fp32_out():
+    d = synth.tiny()
+    xq, wq = _operands_from_f32(d["x"], d["w"])
+    y = _run(xq, wq, torch.float32)
+    y_ref, a_ref = Q.gemm(xq, wq)
+    ok, worst = Q.check_gemm_f32(y, y_ref, a_ref)
+    assert ok, f"worst error / bound = {worst}"
+    # much tighter than the bound in practice (fp32 accumulation of exact products)
+    assert np.max(np.abs(y - y_ref) / np.maximum(a_ref, 1e-30)) < 2e-6
+
+
+def test_tiny_bf16_out_and_amax():
+    d = synth.tiny()
+    xq, wq = _operands_from_f32(d["x"], d["w"])
+    y, amax = _run(xq, wq, torch.bfloat16, amax=True)
+    y_ref, a_ref = Q.gemm(xq, wq)
+    ok, n_clause, n_fail = Q.check_gemm_bf16(y, y_ref, a_ref)
+    assert ok, (n_clause, n_fail)
+    assert amax == np.max(np.abs(y))
+
+
+@pytest.mark.parametrize("lx,lw", [(nv.SCALES_ROWMAJOR, nv.SCALES_ROWMAJOR),
+                                   (nv.SCALES_TILED, nv.SCALES_ROWMAJOR)])
+def test_scale_layouts(lx, lw):
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((256, 512)).astype(np.float32)
+    w = (rng.standard_normal((384, 512)) * 0.02).astype(np.float32)
+    xq, wq = _operands_from_f32(x, w)
+    y = _run(xq, wq, torch.float32, lx, lw)
+    y_ref, a_ref = Q.gemm(xq, wq)
+    assert Q.check_gemm_f32(y, y_ref, a_ref)[0]
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 200, 192), (1, 1, 64), (257, 193, 128), (64, 520, 64)])
+def test_ragged_shapes(m, n, k):
+    rng = np.random.default_rng(m * 7 + n)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    w = rng.standard_normal((n, k)).astype(np.float32)
+    xq, wq = _operands_from_f32(x, w)
+    y = _run(xq, wq, torch.float32, nv.SCALES_ROWMAJOR, nv.SCALES_ROWMAJOR)
+    y_ref, a_ref = Q.gemm(xq, wq)
+    assert Q.check_gemm_f32(y, y_ref, a_ref)[0]
+    yb = _run(xq, wq, torch.bfloat16, nv.SCALES_ROWMAJOR, nv.SCALES_ROWMAJOR)
+    assert Q.check_gemm_bf16(yb, y_ref, a_ref)[0]
+
+
+def test_random_codes_and_all_scale_bytes():
+    # arbitrary code bytes and every scale byte (incl. subnormal scales), odd s_g
+    rng = np.random.default_rng(4)
+    m, n, k = 256, 256, 2048
+    xq = Q.NVFP4(rng.integers(0, 256, (m, k // 2)).astype(np.uint8),
+                 rng.integers(0, 127, (m, k // 16)).astype(np.uint8), float(np.float32(3.1e-3)))
+    wq = Q.NVFP4(rng.integers(0, 256, (n, k // 2)).astype(np.uint8),
+                 rng.integers(0, 127, (n, k // 16)).astype(np.uint8), float(np.float32(0.77)))
+    y = _run(xq, wq, torch.float32)
+    y_ref, a_ref = Q.gemm(xq, wq)
+    assert Q.check_gemm_f32(y, y_ref, a_ref)[0]
+
+
+def test_integer_case_is_exact():
+    # s_g = 1, all scales 1.0: every output is a small integer combination, exact in fp32
+    rng = np.random.default_rng(8)
+    m, n, k = 256, 384, 512
+    xq = Q.NVFP4(rng.integers(0, 256, (m, k // 2)).astype(np.uint8),
+                 np.full((m, k // 16), 0x38, np.uint8), 1.0)
+    wq = Q.NVFP4(rng.integers(0, 256, (n, k // 2)).astype(np.uint8),
+                 np.full((n, k // 16), 0x38, np.uint8), 1.0)
+    y = _run(xq, wq, torch.float32)
+    y_ref, _ = Q.gemm(xq, wq)
+    assert np.array_equal(y, y_ref)
+
+
+def test_attn_proj_reduced():
+    d = synth.attn_proj(m=512, k=3072, n=768)
+    xq = Q.quantize(F.bf16_bits_to_f64(d["x"]))
+    wq = Q.quantize(F.bf16_bits_to_f64(d["w"]))
+    y = _run(xq, wq, torch.bfloat16)
+    y_ref, a_ref = Q.gemm(xq, wq)
+    ok, n_clause, n_fail = Q.check_gemm_bf16(y, y_ref, a_ref)
+    assert ok, (n_clause, n_fail)
+
+
+def test_attn_proj_end_to_end_on_device():
+    # quantize on the GPU, then GEMM on the GPU; the quantized bytes match the
+    # oracle's (checked elsewhere), so the product is checked against the oracle
+    d = synth.attn_proj(m=512, k=3072, n=512)
+    xt = nv.nvfp4_quantize(bf16_tensor(d["x"]))
+    wt = nv.nvfp4_quantize(bf16_tensor(d["w"]))
+    y = nv.nvfp4_gemm_w4a4(xt, wt, torch.bfloat16).float().cpu().numpy().astype(np.float64)
+    xq = Q.quantize(F.bf16_bits_to_f64(d["x"]))
+    wq = Q.quantize(F.bf16_bits_to_f64(d["w"]))
+    y_ref, a_ref = Q.gemm(xq, wq)
+    assert Q.check_gemm_bf16(y, y_ref, a_ref)[0]
+
+
+@pytest.mark.slow
+def test_attn_proj_full_size_sampled():
+    """4096 x 3072 x 3072, bf16 out, in the launch configuration the bench times:
+    4096 sampled outputs checked against exact dot products."""
+    d = synth.attn_proj()
+    xq = Q.quantize(F.bf16_bits_to_f64(d["x"]))
+    wq = Q.quantize(F.bf16_bits_to_f64(d["w"]))
+    y = _run(xq, wq, torch.bfloat16)
+    rng = np.random.default_rng(0)
+    rows = rng.integers(0, 4096, 4096)
+    cols = rng.integers(0, 3072, 4096)
+    # corners of every tile edge too
+    rows[:8] = [0, 0, 4095, 4095, 255, 256, 2047, 2048]
+    cols[:8] = [0, 3071, 0, 3071, 191, 192, 255, 256]
+    y_ref, a_ref = Q.gemm_pairs(xq, wq, rows, cols)
+    ok, n_clause, n_fail = Q.check_gemm_bf16(y[rows, cols], y_ref, a_ref)
+    assert ok, (n_clause, n_fail)
+
+
+@pytest.mark.slow
+def test_ffn_stage_parity():
+    """FFN pair, reduced M: GEMM1 -> requant with the fused amax -> GEMM2, each stage
+    on oracle-made inputs; the chain on the device checked by properties."""
+    d = synth.ffn_pair(m=256)
+    xq = Q.quantize(F.bf16_bits_to_f64(d["x"]))
+    w1q = Q.quantize(F.bf16_bits_to_f64(d["w1"]))
+    w2q = Q.quantize(F.bf16_bits_to_f64(d["w2"]))
+    # stage 1: GEMM1 with fused amax
+    y1, amax = _run(xq, w1q, torch.bfloat16, amax=True)
+    y1_ref, a1_ref = Q.gemm(xq, w1q)
+    assert Q.check_gemm_bf16(y1, y1_ref, a1_ref)[0]
+    assert amax == np.max(np.abs(y1))
+    # stage 2: requantize the oracle's bf16 Y1 on the device with the given amax
+    y1_bits = F.f64_to_bf16_bits(F.round_f64_to_binary(y1_ref, F.BF16))
+    y1o = F.bf16_bits_to_f64(y1_bits)
+    am = float(np.max(np.abs(y1o)))
+    got = to_oracle(nv.nvfp4_quantize(bf16_tensor(y1_bits),
+                                      amax=torch.tensor([am], dtype=torch.float32, device=dev())))
+    want = Q.quantize(y1o, amax=am)
+    assert got.s_g == want.s_g and np.array_equal(got.scales, want.scales)
+    assert np.array_equal(got.packed, want.packed)
+    # stage 3: GEMM2 on the oracle's NVFP4 Y1
+    y2 = _run(want, w2q, torch.bfloat16)
+    y2_ref, a2_ref = Q.gemm(want, w2q)
+    assert Q.check_gemm_bf16(y2, y2_ref, a2_ref)[0]

@@ -1,0 +1,259 @@
+"""Python binding of the NVFP4 hot path on AMD Instinct MI355X (gfx950).
+
+A thin ctypes layer over ``libnvfp4.so`` (C ABI in ``include/nvfp4.h``).
+Functions carry the C names; they only marshal torch tensors (device memory,
+the current HIP stream) into pointers and sizes.  Every step of the path runs
+in the library's HIP kernels; there is no Python or CPU fallback, and a
+missing or broken library raises at import time.
+
+    import w4a4_gemm_amd as nv
+    xq = nv.nvfp4_quantize(x)                       # NVFP4Tensor
+    y  = nv.nvfp4_gemm_w4a4(xq, wq, torch.bfloat16)
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "NVFP4Tensor", "KVCache", "LIB_PATH",
+    "nvfp4_abi_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_kv_page_bytes",
+    "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm_w4a4",
+    "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks",
+    "SCALES_ROWMAJOR", "SCALES_TILED", "OP_QUANTIZE", "OP_KV_QUANTIZE",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so")
+
+# enums (include/nvfp4.h)
+OK, EINVAL, ESHAPE, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+SCALES_ROWMAJOR, SCALES_TILED = 0, 1
+OP_QUANTIZE, OP_KV_QUANTIZE = 0, 1
+ABI_VERSION = 1
+
+EXPORTS = (
+    "nvfp4_abi_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_kv_page_bytes",
+    "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm_w4a4",
+    "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks",
+)
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("global_scale", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("scale_layout", ctypes.c_int32)]
+
+
+class _KVCache(ctypes.Structure):
+    _fields_ = [("pool", ctypes.c_void_p), ("n_phys_pages", ctypes.c_int64),
+                ("n_layers", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("max_chunks", ctypes.c_int32),
+                ("page_table", ctypes.c_void_p), ("page_chunk", ctypes.c_void_p),
+                ("k_mean", ctypes.c_void_p), ("k_gscale", ctypes.c_void_p),
+                ("v_gscale", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m w4a4_gemm_amd.build` "
+            "(there is no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "nvfp4_abi_version": (ctypes.c_int, []),
+        "nvfp4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "nvfp4_workspace_bytes": (sz, [i32, i64, i64, i64]),
+        "nvfp4_kv_page_bytes": (i64, [i32, i32, i32]),
+        "nvfp4_quantize": (ctypes.c_int, [vp, i32, i64, i64, i64, vp, ctypes.POINTER(_Tensor),
+                                          vp, sz, vp]),
+        "nvfp4_dequantize": (ctypes.c_int, [ctypes.POINTER(_Tensor), vp, i32, i64, vp]),
+        "nvfp4_gemm_w4a4": (ctypes.c_int, [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), vp,
+                                           i32, i64, vp, vp]),
+        "nvfp4_kv_quantize": (ctypes.c_int, [ctypes.POINTER(_KVCache), i32, i32, vp, vp, i64, i64,
+                                             vp, sz, vp]),
+        "nvfp4_kv_dequant_blocks": (ctypes.c_int, [ctypes.POINTER(_KVCache), i32, vp, i32, vp, vp,
+                                                   vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)            # AttributeError if the symbol is missing
+        fn.restype, fn.argtypes = res, args
+    if lib.nvfp4_abi_version() != ABI_VERSION:
+        raise ImportError("libnvfp4.so ABI version mismatch: rebuild the library")
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status, what):
+    if status != OK:
+        msg = _lib.nvfp4_status_string(status).decode()
+        raise RuntimeError(f"{what} failed: status {status} ({msg})")
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else ctypes.c_void_p(0)
+
+
+def _dtype_code(dt):
+    if dt == torch.float32:
+        return F32
+    if dt == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+# ------------------------------------------------------------------ plain calls
+
+
+def nvfp4_abi_version():
+    return _lib.nvfp4_abi_version()
+
+
+def nvfp4_status_string(status):
+    return _lib.nvfp4_status_string(status).decode()
+
+
+def nvfp4_workspace_bytes(op, a, b, c):
+    return int(_lib.nvfp4_workspace_bytes(op, a, b, c))
+
+
+def nvfp4_kv_page_bytes(n_heads, head_dim, page_tokens):
+    return int(_lib.nvfp4_kv_page_bytes(n_heads, head_dim, page_tokens))
+
+
+class NVFP4Tensor:
+    """Device buffers of an NVFP4 tensor [rows x cols]: codes, scale bytes, s_g."""
+
+    def __init__(self, rows, cols, layout=SCALES_TILED, device="cuda", codes=None, scales=None,
+                 global_scale=None):
+        self.rows, self.cols, self.layout = int(rows), int(cols), int(layout)
+        self.codes = codes if codes is not None else torch.empty(
+            (rows, cols // 2), dtype=torch.uint8, device=device)
+        self.scales = scales if scales is not None else torch.empty(
+            (rows * cols // 16,), dtype=torch.uint8, device=device)
+        self.global_scale = global_scale if global_scale is not None else torch.empty(
+            (1,), dtype=torch.float32, device=device)
+
+    def c(self):
+        return _Tensor(self.codes.data_ptr() if self.codes.numel() else 0,
+                       self.scales.data_ptr() if self.scales.numel() else 0,
+                       self.global_scale.data_ptr(), self.rows, self.cols, self.layout)
+
+    @property
+    def shape(self):
+        return self.rows, self.cols
+
+
+def nvfp4_quantize(x, layout=SCALES_TILED, amax=None, out=None, workspace=None, stream=None):
+    """Quantize a 2-D bf16/fp32 CUDA tensor (row stride x.stride(0)) to NVFP4."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    rows, cols = x.shape
+    if out is None:
+        out = NVFP4Tensor(rows, cols, layout, device=x.device)
+    need = nvfp4_workspace_bytes(OP_QUANTIZE, rows, cols, 1 if amax is not None else 0)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    cs = out.c()
+    st = _lib.nvfp4_quantize(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0),
+                             _ptr(amax), ctypes.byref(cs), _ptr(workspace),
+                             workspace.numel() if workspace is not None else 0, _stream(stream))
+    _check(st, "nvfp4_quantize")
+    return out
+
+
+def nvfp4_dequantize(t, dtype=torch.float32, out=None, stream=None):
+    if out is None:
+        out = torch.empty((t.rows, t.cols), dtype=dtype, device=t.codes.device)
+    cs = t.c()
+    st = _lib.nvfp4_dequantize(ctypes.byref(cs), _ptr(out), _dtype_code(out.dtype),
+                               out.stride(0) if out.dim() == 2 else t.cols, _stream(stream))
+    _check(st, "nvfp4_dequantize")
+    return out
+
+
+def nvfp4_gemm_w4a4(x, w, dtype=torch.bfloat16, out=None, y_amax=None, stream=None):
+    """Y = X W^T for NVFP4 X [M x K], W [N x K]."""
+    if out is None:
+        out = torch.empty((x.rows, w.rows), dtype=dtype, device=x.codes.device)
+    xs, ws = x.c(), w.c()
+    st = _lib.nvfp4_gemm_w4a4(ctypes.byref(xs), ctypes.byref(ws), _ptr(out), _dtype_code(out.dtype),
+                              out.stride(0) if out.dim() == 2 else w.rows, _ptr(y_amax),
+                              _stream(stream))
+    _check(st, "nvfp4_gemm_w4a4")
+    return out
+
+
+# ------------------------------------------------------------------ KV cache
+
+
+class KVCache:
+    """Device buffers of a paged NVFP4 KV cache (layout in include/nvfp4.h)."""
+
+    def __init__(self, n_layers, n_heads, head_dim, page_tokens, max_pages, max_chunks,
+                 page_table, n_phys_pages, device="cuda"):
+        self.n_layers, self.n_heads, self.head_dim = n_layers, n_heads, head_dim
+        self.page_tokens, self.max_pages, self.max_chunks = page_tokens, max_pages, max_chunks
+        self.n_phys_pages = n_phys_pages
+        self.page_bytes = nvfp4_kv_page_bytes(n_heads, head_dim, page_tokens)
+        self.pool = torch.zeros((n_phys_pages, self.page_bytes), dtype=torch.uint8, device=device)
+        self.page_table = torch.as_tensor(page_table, dtype=torch.int32).reshape(
+            n_layers, max_pages).to(device).contiguous()
+        self.page_chunk = torch.zeros((n_layers, max_pages, 2), dtype=torch.int32, device=device)
+        self.k_mean = torch.zeros((n_layers, max_chunks, n_heads, head_dim), dtype=torch.float32,
+                                  device=device)
+        self.k_gscale = torch.zeros((n_layers, max_chunks), dtype=torch.float32, device=device)
+        self.v_gscale = torch.zeros((n_layers, max_chunks), dtype=torch.float32, device=device)
+        self._c = _KVCache(self.pool.data_ptr(), n_phys_pages, n_layers, n_heads, head_dim,
+                           page_tokens, max_pages, max_chunks, self.page_table.data_ptr(),
+                           self.page_chunk.data_ptr(), self.k_mean.data_ptr(),
+                           self.k_gscale.data_ptr(), self.v_gscale.data_ptr())
+        self._ws = None
+
+    def c(self):
+        return self._c
+
+    def workspace(self, T):
+        need = nvfp4_workspace_bytes(OP_KV_QUANTIZE, T, self.n_heads, self.head_dim)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.pool.device)
+        return self._ws
+
+
+def nvfp4_kv_quantize(cache, layer, chunk_id, k, v, start_token, workspace=None, stream=None):
+    """Write one chunk (K, V bf16 [T, n_heads, head_dim]) into the cache in place."""
+    T = k.shape[0]
+    if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("K and V must be bf16")
+    if not (k.is_contiguous() and v.is_contiguous()) or k.shape != v.shape:
+        raise ValueError("K and V must be contiguous [T, n_heads, head_dim] of the same shape")
+    if tuple(k.shape[1:]) != (cache.n_heads, cache.head_dim):
+        raise ValueError("K shape does not match the cache")
+    ws = workspace if workspace is not None else cache.workspace(T)
+    st = _lib.nvfp4_kv_quantize(ctypes.byref(cache.c()), layer, chunk_id, _ptr(k), _ptr(v), T,
+                                start_token, _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "nvfp4_kv_quantize")
+
+
+def nvfp4_kv_dequant_blocks(cache, layer, logical_pages, k_out=None, v_out=None, stream=None):
+    """Dequantize the listed logical pages -> (K^, V^) bf16 [n*page_tokens, H, D]."""
+    n = logical_pages.numel()
+    shape = (n * cache.page_tokens, cache.n_heads, cache.head_dim)
+    if k_out is None:
+        k_out = torch.empty(shape, dtype=torch.bfloat16, device=cache.pool.device)
+    if v_out is None:
+        v_out = torch.empty(shape, dtype=torch.bfloat16, device=cache.pool.device)
+    st = _lib.nvfp4_kv_dequant_blocks(ctypes.byref(cache.c()), layer, _ptr(logical_pages), n,
+                                      _ptr(k_out), _ptr(v_out), _stream(stream))
+    _check(st, "nvfp4_kv_dequant_blocks")
+    return k_out, v_out

@@ -1,0 +1,75 @@
+"""Build the NVFP4 HIP library in-tree: ``w4a4_gemm_amd/libnvfp4.so`` (gfx950 only).
+
+Every source is compiled with hipcc for ``--offload-arch=gfx950`` and linked
+into one shared library that exports the C ABI of ``include/nvfp4.h``.
+
+Flags:
+* ``-Xclang -target-feature -Xclang -packed-fp32-ops`` -- no packed fp32
+  instructions are generated (the host pass warns that it does not know the
+  feature; that warning is harmless).
+* ``-fno-gpu-flush-denormals-to-zero`` -- fp32 subnormals are kept, which the
+  exact rounding in the kernels relies on.
+
+Usage:  python -m w4a4_gemm_amd.build  [-v]
+"""
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libnvfp4.so")
+SOURCES = ["capi.cpp", "quant.hip", "kv.hip", "gemm.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+COMMON = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-fno-gpu-flush-denormals-to-zero",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    f"-I{INCLUDE}",
+    f"-I{CSRC}",
+]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in (p.stderr or "").splitlines() if noise not in l)
+    if p.returncode != 0:
+        raise RuntimeError(f"command failed ({p.returncode}): {' '.join(cmd)}\n{err}")
+    if verbose and err.strip():
+        print(err)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libnvfp4.so; returns the library path."""
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmds.append([HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

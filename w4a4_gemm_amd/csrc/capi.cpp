@@ -1,0 +1,195 @@
+// C ABI of the NVFP4 library (declared in include/nvfp4.h): argument checks,
+// status codes and dispatch to the gfx950 kernels.  No allocation, no host
+// synchronisation, no library state.
+
+#include "nvfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+
+namespace {
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Launch errors are sticky per thread in HIP; clear any stale error first so
+// that a failure is attributed to this call.
+inline int finish() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+}
+
+inline hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+int check_tensor(const nvfp4_tensor_t* t) {
+  if (!t) return NVFP4_EINVAL;
+  if (t->rows < 0 || t->cols < 0) return NVFP4_EINVAL;
+  if (t->scale_layout != NVFP4_SCALES_ROWMAJOR && t->scale_layout != NVFP4_SCALES_TILED)
+    return NVFP4_EINVAL;
+  if (t->cols % 16) return NVFP4_ESHAPE;
+  if (!t->global_scale) return NVFP4_EINVAL;
+  if (t->rows > 0 && t->cols > 0 && (!t->codes || !t->scales)) return NVFP4_EINVAL;
+  if (t->scale_layout == NVFP4_SCALES_TILED && (t->rows % 128 || t->cols % 64))
+    return NVFP4_ESHAPE;
+  if (!aligned(t->codes, 16) || !aligned(t->scales, 4) || !aligned(t->global_scale, 4))
+    return NVFP4_ESHAPE;
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_EINVAL: return "invalid argument (null pointer, bad enum or negative size)";
+    case NVFP4_ESHAPE: return "unsupported shape, stride or alignment";
+    case NVFP4_EWORKSPACE: return "workspace missing or too small";
+    case NVFP4_EHIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t nvfp4_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c) {
+  switch (op) {
+    case NVFP4_OP_QUANTIZE: return nvfp4::quantize_workspace_bytes(a, b, c != 0);
+    case NVFP4_OP_KV_QUANTIZE: return nvfp4::kv_quantize_workspace_bytes(a, b, c);
+    default: return 0;
+  }
+}
+
+int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                   const float* amax, const nvfp4_tensor_t* out, void* workspace,
+                   size_t ws_bytes, void* stream) {
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (rows < 0 || cols < 0) return NVFP4_EINVAL;
+  int st = check_tensor(out);
+  if (st) return st;
+  if (out->rows != rows || out->cols != cols) return NVFP4_ESHAPE;
+  const int64_t elem = x_dtype == NVFP4_BF16 ? 2 : 4;
+  if (ld_x < cols || (ld_x * elem) % 16) return NVFP4_ESHAPE;
+  if (rows > 0 && cols > 0 && !x) return NVFP4_EINVAL;
+  if (!aligned(x, 16)) return NVFP4_ESHAPE;
+  if (amax && !aligned(amax, 4)) return NVFP4_ESHAPE;
+  const size_t need = nvfp4::quantize_workspace_bytes(rows, cols, amax != nullptr);
+  if (need && (!workspace || ws_bytes < need || !aligned(workspace, 256))) return NVFP4_EWORKSPACE;
+  (void)hipGetLastError();
+  nvfp4::launch_quantize(x, x_dtype == NVFP4_BF16, rows, cols, ld_x, amax, out->codes,
+                         out->scales, out->scale_layout == NVFP4_SCALES_TILED,
+                         out->global_scale, workspace, as_stream(stream));
+  return finish();
+}
+
+int nvfp4_dequantize(const nvfp4_tensor_t* in, void* y, int32_t y_dtype, int64_t ld_y,
+                     void* stream) {
+  int st = check_tensor(in);
+  if (st) return st;
+  if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  const int64_t elem = y_dtype == NVFP4_BF16 ? 2 : 4;
+  if (ld_y < in->cols || (ld_y * elem) % 16) return NVFP4_ESHAPE;
+  if (in->rows > 0 && in->cols > 0 && !y) return NVFP4_EINVAL;
+  if (!aligned(y, 16)) return NVFP4_ESHAPE;
+  (void)hipGetLastError();
+  nvfp4::launch_dequantize(in->codes, in->scales, in->scale_layout == NVFP4_SCALES_TILED,
+                           in->global_scale, in->rows, in->cols, y, y_dtype == NVFP4_BF16, ld_y,
+                           as_stream(stream));
+  return finish();
+}
+
+int nvfp4_gemm_w4a4(const nvfp4_tensor_t* x, const nvfp4_tensor_t* w, void* y, int32_t y_dtype,
+                    int64_t ld_y, float* y_amax, void* stream) {
+  int st = check_tensor(x);
+  if (st) return st;
+  st = check_tensor(w);
+  if (st) return st;
+  if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (x->cols != w->cols) return NVFP4_ESHAPE;
+  const int64_t M = x->rows, N = w->rows, K = x->cols;
+  if (K % 64) return NVFP4_ESHAPE;
+  if (ld_y < N) return NVFP4_ESHAPE;
+  if (M > 0 && N > 0 && !y) return NVFP4_EINVAL;
+  if (!aligned(y, 4) || (y_amax && !aligned(y_amax, 4))) return NVFP4_ESHAPE;
+  if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31)) return NVFP4_ESHAPE;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  (void)hipGetLastError();
+  nvfp4::launch_gemm(x->codes, x->scales, x->scale_layout == NVFP4_SCALES_TILED, x->global_scale,
+                     w->codes, w->scales, w->scale_layout == NVFP4_SCALES_TILED, w->global_scale,
+                     M, N, K, y, y_dtype == NVFP4_BF16, ld_y, y_amax, as_stream(stream));
+  return finish();
+}
+
+int64_t nvfp4_kv_page_bytes(int32_t n_heads, int32_t head_dim, int32_t page_tokens) {
+  if (n_heads <= 0 || head_dim <= 0 || head_dim % 16 || page_tokens <= 0) return 0;
+  return (int64_t)2 * n_heads * page_tokens * (head_dim / 2 + head_dim / 16);
+}
+
+static int check_cache(const nvfp4_kv_cache_t* c, int32_t layer, nvfp4::KvGeom* g) {
+  if (!c || !c->pool || !c->page_table || !c->page_chunk || !c->k_mean || !c->k_gscale ||
+      !c->v_gscale)
+    return NVFP4_EINVAL;
+  if (c->n_layers <= 0 || c->n_heads <= 0 || c->head_dim <= 0 || c->page_tokens <= 0 ||
+      c->max_pages <= 0 || c->max_chunks <= 0 || c->n_phys_pages <= 0)
+    return NVFP4_EINVAL;
+  if (c->head_dim % 16 || c->head_dim > 256) return NVFP4_ESHAPE;
+  if (layer < 0 || layer >= c->n_layers) return NVFP4_ESHAPE;
+  if (!aligned(c->pool, 16) || !aligned(c->k_mean, 16)) return NVFP4_ESHAPE;
+  if (nvfp4_kv_page_bytes(c->n_heads, c->head_dim, c->page_tokens) % 16) return NVFP4_ESHAPE;
+  if (c->n_heads > 65535) return NVFP4_ESHAPE;
+  g->pool = c->pool;
+  g->n_heads = c->n_heads;
+  g->head_dim = c->head_dim;
+  g->page_tokens = c->page_tokens;
+  g->max_pages = c->max_pages;
+  g->max_chunks = c->max_chunks;
+  g->page_table = c->page_table + (int64_t)layer * c->max_pages;
+  g->page_chunk = c->page_chunk + (int64_t)layer * c->max_pages * 2;
+  g->k_mean = c->k_mean + (int64_t)layer * c->max_chunks * c->n_heads * c->head_dim;
+  g->k_gscale = c->k_gscale + (int64_t)layer * c->max_chunks;
+  g->v_gscale = c->v_gscale + (int64_t)layer * c->max_chunks;
+  g->page_bytes = nvfp4_kv_page_bytes(c->n_heads, c->head_dim, c->page_tokens);
+  g->n_phys_pages = c->n_phys_pages;
+  return NVFP4_OK;
+}
+
+int nvfp4_kv_quantize(const nvfp4_kv_cache_t* cache, int32_t layer, int32_t chunk_id,
+                      const void* k_bf16, const void* v_bf16, int64_t T, int64_t start_token,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  nvfp4::KvGeom g;
+  int st = check_cache(cache, layer, &g);
+  if (st) return st;
+  if (T <= 0 || start_token < 0 || !k_bf16 || !v_bf16) return NVFP4_EINVAL;
+  if (!aligned(k_bf16, 16) || !aligned(v_bf16, 16)) return NVFP4_ESHAPE;
+  if (chunk_id < 0 || chunk_id >= cache->max_chunks) return NVFP4_ESHAPE;
+  if (T < cache->page_tokens && chunk_id != 0) return NVFP4_ESHAPE;
+  if ((start_token + T + cache->page_tokens - 1) / cache->page_tokens > cache->max_pages)
+    return NVFP4_ESHAPE;
+  if (T >= (int64_t(1) << 31)) return NVFP4_ESHAPE;
+  const size_t need = nvfp4::kv_quantize_workspace_bytes(T, cache->n_heads, cache->head_dim);
+  if (!workspace || ws_bytes < need || !aligned(workspace, 256)) return NVFP4_EWORKSPACE;
+  (void)hipGetLastError();
+  nvfp4::launch_kv_quantize(g, chunk_id, (const uint16_t*)k_bf16, (const uint16_t*)v_bf16, T,
+                            start_token, workspace, as_stream(stream));
+  return finish();
+}
+
+int nvfp4_kv_dequant_blocks(const nvfp4_kv_cache_t* cache, int32_t layer,
+                            const int32_t* logical_pages, int32_t n_pages, void* k_out,
+                            void* v_out, void* stream) {
+  nvfp4::KvGeom g;
+  int st = check_cache(cache, layer, &g);
+  if (st) return st;
+  if (n_pages < 0) return NVFP4_EINVAL;
+  if (n_pages == 0) return NVFP4_OK;
+  if (!logical_pages || !k_out || !v_out) return NVFP4_EINVAL;
+  if (!aligned(k_out, 16) || !aligned(v_out, 16) || !aligned(logical_pages, 4))
+    return NVFP4_ESHAPE;
+  (void)hipGetLastError();
+  nvfp4::launch_kv_dequant(g, logical_pages, n_pages, (uint16_t*)k_out, (uint16_t*)v_out,
+                           as_stream(stream));
+  return finish();
+}
+
+}  // extern "C"

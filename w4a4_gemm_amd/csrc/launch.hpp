@@ -1,0 +1,53 @@
+// Host-side launchers of the NVFP4 kernels.  Arguments are validated by the
+// C ABI layer (capi.cpp) before any of these is called; each launcher only
+// picks the launch geometry and enqueues on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// ---- quantize / dequantize (quant.hip)
+constexpr int kAmaxPartials = 1024;   // max partial maxima written by the amax pass
+
+// Workspace floats used by the amax pass (partials), 256-byte rounded.
+size_t quantize_workspace_bytes(int64_t rows, int64_t cols, bool has_amax);
+
+void launch_quantize(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ld,
+                     const float* amax, uint8_t* codes, uint8_t* scales, bool tiled,
+                     float* gscale, void* workspace, hipStream_t stream);
+
+void launch_dequantize(const uint8_t* codes, const uint8_t* scales, bool tiled,
+                       const float* gscale, int64_t rows, int64_t cols, void* y, bool y_bf16,
+                       int64_t ld_y, hipStream_t stream);
+
+// ---- W4A4 GEMM (gemm.hip)
+void launch_gemm(const uint8_t* xc, const uint8_t* xs, bool x_tiled, const float* xg,
+                 const uint8_t* wc, const uint8_t* ws, bool w_tiled, const float* wg,
+                 int64_t M, int64_t N, int64_t K, void* y, bool y_bf16, int64_t ld_y,
+                 float* y_amax, hipStream_t stream);
+
+// ---- KV cache (kv.hip)
+struct KvGeom {
+  uint8_t* pool;
+  int32_t n_heads, head_dim, page_tokens, max_pages, max_chunks;
+  const int32_t* page_table;  // this layer's row
+  int32_t* page_chunk;        // this layer's row
+  float* k_mean;              // this layer's [max_chunks][H][D]
+  float* k_gscale;            // this layer's [max_chunks]
+  float* v_gscale;
+  int64_t page_bytes;
+  int64_t n_phys_pages;
+};
+
+size_t kv_quantize_workspace_bytes(int64_t T, int64_t H, int64_t D);
+
+void launch_kv_quantize(const KvGeom& g, int32_t chunk_id, const uint16_t* k, const uint16_t* v,
+                        int64_t T, int64_t start_token, void* workspace, hipStream_t stream);
+
+void launch_kv_dequant(const KvGeom& g, const int32_t* logical_pages, int32_t n_pages,
+                       uint16_t* k_out, uint16_t* v_out, hipStream_t stream);
+
+}  // namespace nvfp4

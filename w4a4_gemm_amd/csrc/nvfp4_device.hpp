@@ -1,0 +1,232 @@
+// Device-side NVFP4 helpers for gfx950 (CDNA4).
+//
+// NVFP4 (techwalker.com LongLive-2.0 report summary, section 一): E2M1 4-bit
+// values, one E4M3 scale per 16 values, one fp32 scale per tensor.  Every
+// rounding below reproduces a single round-to-nearest-even of the exact real
+// value; the argument for each shortcut is stated where it is used.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 16;                  // values per E4M3 block scale
+
+// ------------------------------------------------------------------ bit views
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// f32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  __bf16 b = (__bf16)f;
+  uint16_t s;
+  __builtin_memcpy(&s, &b, 2);
+  return s;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ------------------------------------------------------------------ scales
+
+// Value of an E4M3FN byte in 0x00..0x7E (bias 7; exponent field 0 is m/8 * 2^-6).
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  float normal = __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1 + m/8) 2^(e-7)
+  float sub = (float)m * 0x1p-9f;                                   // m 2^-9
+  return e ? normal : sub;
+}
+
+// s_g = RN32(amax / 2688), or 1 when amax == 0.  __fdiv_rn is the correctly
+// rounded fp32 quotient.
+__device__ __forceinline__ float global_scale(float amax) {
+  return amax == 0.0f ? 1.0f : __fdiv_rn(amax, 2688.0f);
+}
+
+// E4M3 byte nearest to the exact quotient t = b / (6 s_g) (ties to even,
+// saturating at 448).
+//
+// t64 = RN64(b / (6 s_g)) is on the same side of every E4M3 midpoint as the
+// exact t, and equals a midpoint only when t does: b has 24 significant bits
+// and 6 s_g M (M a midpoint, 5 bits) has at most 31, so a nonzero b - 6 s_g M
+// is at least 2^-33 relative, far above fp64's 2^-53 division error.  Rounding
+// t64 to 3 mantissa bits with RNE therefore gives the exact answer.
+__device__ __forceinline__ uint32_t e4m3_block_scale(float b, double six_sg) {
+  double t = (double)b / six_sg;
+  if (t >= 464.0) return 0x7Eu;             // [448, 464] rounds to 448; beyond saturates
+  if (t < 0x1p-6) {                         // subnormal range: m = RNE(t * 2^9) in 0..8
+    return (uint32_t)__builtin_rint(t * 512.0);   // 8 is byte 0x08 = 2^-6
+  }
+  uint64_t bits = (uint64_t)__double_as_longlong(t);
+  bits += (1ull << 48) - 1ull + ((bits >> 49) & 1ull);  // RNE to 3 fraction bits
+  return (uint32_t)(bits >> 49) - ((1023u - 7u) << 3);  // rebias exponent 1023 -> 7
+}
+
+// ------------------------------------------------------------------ E2M1 encoding
+
+// Per-block encoder state.  Codes come from the hardware fp32 -> E2M1
+// conversion (RNE, saturating at 6, sign kept; checked exhaustively against
+// the exact rule) applied to y = x * c for two multipliers that bracket the
+// exact 1 / (s_b s_g) from below and above:
+//   c_lo = RN32(inv (1 - 2^-20)),  c_hi = RN32(inv (1 + 2^-20)),  inv = RN64(1 / (s_b s_g))
+// so |x| c_lo (1 + 2^-24) < r < |x| c_hi (1 - 2^-24) with r = |x| / (s_b s_g).
+// The conversion is monotone, so equal codes for both are the code of r.
+// Where they differ (r within 2^-20 of an E2M1 midpoint M, or exactly on it)
+// the exact comparison  |x| - M s_b s_g  decides: M s_b has at most 7 bits, so
+// one fp32 FMA gives that difference with a single rounding and an exact sign.
+//
+// `pre` (1 or 2^64) scales x up for tensors with s_g < 2^-100 so that c stays
+// inside the fp32 range; the scaling is exact and cancels in the codes.
+struct BlockEnc {
+  float c_lo, c_hi;   // multipliers (0 when s_b == 0: every code is sign | 0)
+  float msb_neg[7];   // -(M_k s_b) for the 7 E2M1 midpoints
+  float sg_pre;       // s_g * pre
+};
+
+__device__ __forceinline__ BlockEnc make_block_enc(uint32_t sb_byte, float s_b, float s_g,
+                                                   float pre) {
+  BlockEnc e;
+  if (sb_byte == 0) {
+    e.c_lo = 0.0f;
+    e.c_hi = 0.0f;
+  } else {
+    double inv = 1.0 / ((double)s_b * (double)s_g * (double)pre);   // product exact in fp64
+    e.c_lo = (float)(inv * (1.0 - 0x1p-20));
+    e.c_hi = (float)(inv * (1.0 + 0x1p-20));
+  }
+  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+#pragma unroll
+  for (int k = 0; k < 7; ++k) e.msb_neg[k] = -(mids[k] * s_b);
+  e.sg_pre = s_g * pre;
+  return e;
+}
+
+// Codes of 8 values (x already multiplied by `pre`) -> 8 nibbles, value j in
+// bits 4j+3..4j (so byte i holds values 2i, 2i+1 with the even one low).
+__device__ __forceinline__ uint32_t encode8(const float* x, const BlockEnc& e) {
+  uint32_t lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x[0] * e.c_lo, x[1] * e.c_lo, 1.0f, 0);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[0] * e.c_hi, x[1] * e.c_hi, 1.0f, 0);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x[2] * e.c_lo, x[3] * e.c_lo, 1.0f, 1);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[2] * e.c_hi, x[3] * e.c_hi, 1.0f, 1);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x[4] * e.c_lo, x[5] * e.c_lo, 1.0f, 2);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[4] * e.c_hi, x[5] * e.c_hi, 1.0f, 2);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x[6] * e.c_lo, x[7] * e.c_lo, 1.0f, 3);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[6] * e.c_hi, x[7] * e.c_hi, 1.0f, 3);
+  if (__builtin_expect(lo != hi, 0)) {
+    // resolve each differing nibble exactly
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t cl = (lo >> (4 * j)) & 0xFu, ch = (hi >> (4 * j)) & 0xFu;
+      if (cl != ch) {
+        uint32_t ml = cl & 7u;                          // magnitudes ml and ml + 1
+        float nms = e.msb_neg[0];
+#pragma unroll
+        for (int k = 1; k < 7; ++k) nms = (ml == (uint32_t)k) ? e.msb_neg[k] : nms;
+        float d = __builtin_fmaf(nms, e.sg_pre, __builtin_fabsf(x[j]));   // sign exact
+        bool up = d > 0.0f || (d == 0.0f && (ml & 1u));  // tie: to the even magnitude
+        uint32_t c = up ? ch : cl;
+        lo = (lo & ~(0xFu << (4 * j))) | (c << (4 * j));
+      }
+    }
+  }
+  return lo;
+}
+
+// ------------------------------------------------------------------ 64-value groups
+
+// Quantize `nblk` (1..4) blocks held in v[0 .. 16*nblk) into codes and scale bytes.
+template <bool kPre>
+__device__ __forceinline__ void quantize_group(float* v, int nblk, float s_g, double six_sg,
+                                               uint32_t* code_words, uint32_t& scale_word) {
+  const float pre = kPre ? 0x1p64f : 1.0f;
+  scale_word = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    if (b < nblk) {
+      float bm = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) bm = fmaxf(bm, __builtin_fabsf(v[16 * b + j]));
+      const uint32_t sb = e4m3_block_scale(bm, six_sg);
+      const BlockEnc enc = make_block_enc(sb, e4m3_value(sb), s_g, pre);
+      if (kPre) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[16 * b + j] *= pre;
+      }
+      code_words[2 * b] = encode8(v + 16 * b, enc);
+      code_words[2 * b + 1] = encode8(v + 16 * b + 8, enc);
+      scale_word |= sb << (8 * b);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ decoding
+
+// q (E2M1 value) for the two nibbles of byte `sel` of w, as fp32 (exact).
+__device__ __forceinline__ f32x2 e2m1_pair(uint32_t w, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  }
+}
+
+// RN_bf16(a * g) with one rounding of the exact product (a has <= 6
+// significant bits, g is fp32): p = RN32(a g) gives the right bf16 rounding
+// unless p is exactly a bf16 midpoint; then the exact residual a g - p (one
+// FMA, exact) says on which side the true product lies, and p is moved one
+// fp32 ulp toward it before the RNE conversion.
+__device__ __forceinline__ float mul_for_bf16(float a, float g) {
+  float p = a * g;
+  uint32_t pb = __float_as_uint(p);
+  if (__builtin_expect((pb & 0xFFFFu) == 0x8000u, 0)) {
+    float r = __builtin_fmaf(a, g, -p);
+    if (r != 0.0f) {
+      bool away = (r > 0.0f) == (p > 0.0f);          // exact value further from zero
+      p = __uint_as_float(away ? pb + 1u : pb - 1u);
+    }
+  }
+  return p;
+}
+
+// RN_bf16(a * g + mu) with one rounding of the exact value.  f = RN32(a g + mu)
+// (one FMA) decides correctly unless it is exactly a bf16 midpoint; then the
+// exact value is compared with f in fp64: A = a g is exact in fp64 (30 bits),
+// s + e = A + mu exactly (TwoSum), and (s - f) is exact (Sterbenz), so the sign
+// of (s - f) + e is the sign of the true offset from the midpoint.
+__device__ __forceinline__ float fma_for_bf16(float a, float g, float mu) {
+  float f = __builtin_fmaf(a, g, mu);
+  uint32_t fb = __float_as_uint(f);
+  if (__builtin_expect((fb & 0xFFFFu) == 0x8000u, 0)) {
+    double A = (double)a * (double)g;
+    double m = (double)mu;
+    double s = A + m;
+    double bb = s - A;
+    double e = (A - (s - bb)) + (m - bb);
+    double off = (s - (double)f) + e;
+    if (off != 0.0) {
+      bool away = (off > 0.0) == (f > 0.0f);
+      f = __uint_as_float(away ? fb + 1u : fb - 1u);
+    }
+  }
+  return f;
+}
+
+// ------------------------------------------------------------------ reductions
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace nvfp4
