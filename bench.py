@@ -1,0 +1,323 @@
+"""Benchmark of the NVFP4 hot path on one MI355X.
+
+One step is one pass of the whole hot path over resident synthetic inputs:
+
+  attn proj   quantize X bf16 [4096 x 3072] (amax + fused scale/encode), then
+              W4A4 GEMM with the pre-quantized W [3072 x 3072] -> bf16 [4096 x 3072]
+  dequantize  X's NVFP4 back to bf16 [4096 x 3072]
+  ffn pair    quantize X [8192 x 3072]; GEMM1 with W1 [14336 x 3072] -> Y1 bf16 with
+              the fused output amax; requantize Y1 (one read, amax given); GEMM2
+              with W2 [3072 x 14336] -> bf16 [8192 x 3072]
+  kv write    one layer's new chunk K, V bf16 [7040 x 24 x 128]: K mean, K', NVFP4
+              into 256-token pages of a shuffled page table
+  kv read     30 layers x 65536 cached tokens: the window of every layer (4 sink
+              pages + the most recent 16384 tokens = 68 pages) dequantized to bf16
+              with the K means added back, one launch per layer
+
+The metric is the whole step as a percentage of the MI355X roofline: the time
+the step's algorithmic work takes at the roofline (HBM 8 TB/s for the
+bandwidth kernels -- one read of every input and one write of every output --
+and the 2.5 PFLOP/s dense bf16 MFMA peak for the GEMMs) divided by the
+measured step time.  Per-op rates (GB/s, TFLOP/s) and fractions are reported
+alongside, plus the roofline of the dominant kernel (the FFN GEMM1 launch)
+and the CPU oracle's rate on a bounded sample of the same work.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_BPS = 8.0e12               # MI355X HBM3E peak, bytes/s
+MFMA_BF16_FLOPS = 2.5e15       # MI355X dense bf16 MFMA peak, FLOP/s
+METRIC = "W4A4 GEMM TFLOPS + quant/dequant/KV GB/s, as % of MI355X roofline"
+
+NV_ELEM = 0.5625               # NVFP4 bytes per element (4-bit code + E4M3 per 16)
+
+
+# ------------------------------------------------------------------ workload accounting
+
+def op_table():
+    """Algorithmic bytes / FLOPs of every op in one step."""
+    a_m, a_k, a_n = 4096, 3072, 3072
+    f_m, f_d, f_f = 8192, 3072, 14336
+    kv_t, kv_h, kv_d = 7040, 24, 128
+    layers, win_pages, page = 30, 68, 256
+    page_bytes = 2 * kv_h * page * (kv_d // 2 + kv_d // 16)
+    kv_elems = kv_t * kv_h * kv_d
+    win_elems = win_pages * page * kv_h * kv_d          # per K (or V) per layer
+    return {
+        "attn_quantize": {"bytes": a_m * a_k * (2 + NV_ELEM) + 4},
+        "attn_gemm": {"flops": 2 * a_m * a_n * a_k},
+        "attn_dequantize": {"bytes": a_m * a_k * (NV_ELEM + 2) + 4},
+        "ffn_quantize": {"bytes": f_m * f_d * (2 + NV_ELEM) + 4},
+        "ffn_gemm1": {"flops": 2 * f_m * f_f * f_d},
+        "ffn_requantize": {"bytes": f_m * f_f * (2 + NV_ELEM) + 4},
+        "ffn_gemm2": {"flops": 2 * f_m * f_d * f_f},
+        "kv_write": {"bytes": 2 * kv_elems * 2 + 2 * kv_elems * NV_ELEM + kv_h * kv_d * 4 + 8},
+        "kv_read": {"bytes": layers * (win_pages * page_bytes + 2 * win_elems * 2),
+                    "compressed_bytes": layers * win_pages * page_bytes},
+    }
+
+
+def roofline_seconds(op):
+    if "flops" in op:
+        return op["flops"] / MFMA_BF16_FLOPS
+    return op["bytes"] / HBM_BPS
+
+
+# ------------------------------------------------------------------ GPU step
+
+class Workload:
+    def __init__(self, dev):
+        import torch
+        import synth
+        import w4a4_gemm_amd as nv
+        self.nv, self.torch, self.dev = nv, torch, dev
+
+        def bf16(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+
+        a = synth.attn_proj()
+        self.ax = bf16(a["x"])
+        self.aw = nv.nvfp4_quantize(bf16(a["w"]))                 # weights pre-quantized
+        self.axq = nv.NVFP4Tensor(4096, 3072, nv.SCALES_TILED, device=dev)
+        self.ay = torch.empty((4096, 3072), dtype=torch.bfloat16, device=dev)
+        self.adq = torch.empty((4096, 3072), dtype=torch.bfloat16, device=dev)
+        self.aws = torch.empty(nv.nvfp4_workspace_bytes(nv.OP_QUANTIZE, 4096, 3072, 0),
+                               dtype=torch.uint8, device=dev)
+        del a
+
+        f = synth.ffn_pair()
+        self.fx = bf16(f["x"])
+        self.fw1 = nv.nvfp4_quantize(bf16(f["w1"]))
+        self.fw2 = nv.nvfp4_quantize(bf16(f["w2"]))
+        del f
+        self.fxq = nv.NVFP4Tensor(8192, 3072, nv.SCALES_TILED, device=dev)
+        self.fy1 = torch.empty((8192, 14336), dtype=torch.bfloat16, device=dev)
+        self.fy1q = nv.NVFP4Tensor(8192, 14336, nv.SCALES_TILED, device=dev)
+        self.fy2 = torch.empty((8192, 3072), dtype=torch.bfloat16, device=dev)
+        self.famax = torch.zeros(1, dtype=torch.float32, device=dev)
+        self.fws = torch.empty(nv.nvfp4_workspace_bytes(nv.OP_QUANTIZE, 8192, 3072, 0),
+                               dtype=torch.uint8, device=dev)
+
+        kb, vb = synth.kv_chunk()
+        self.kv_k, self.kv_v = bf16(kb), bf16(vb)
+        table = synth.page_permutation(28, 33)[None, :]
+        self.kv_w = nv.KVCache(1, 24, 128, 256, 28, 1, table, 28, device=dev)
+        self.kv_ws = self.kv_w.workspace(7040)
+
+        r = synth.LongContextKV()
+        self.lc = nv.KVCache(r.L, r.H, r.D, r.P, r.pages_per_layer, len(r.chunks), r.page_table,
+                             r.n_phys, device=dev)
+        for layer in range(r.L):
+            for c in range(len(r.chunks)):
+                start, k, v = r.chunk_torch(layer, c, dev)
+                nv.nvfp4_kv_quantize(self.lc, layer, c, k, v, start, workspace=self.kv_ws)
+        self.lc_layers = r.L
+        self.window = torch.tensor(r.window(), dtype=torch.int32, device=dev)
+        n = self.window.numel() * r.P
+        self.kh = torch.empty((n, r.H, r.D), dtype=torch.bfloat16, device=dev)
+        self.vh = torch.empty((n, r.H, r.D), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self, ev=None):
+        """One pass of the hot path.  ``ev(name)`` records a timing event boundary."""
+        nv, torch = self.nv, self.torch
+        mark = ev or (lambda name: None)
+        mark("attn_quantize")
+        nv.nvfp4_quantize(self.ax, out=self.axq, workspace=self.aws)
+        mark("attn_gemm")
+        nv.nvfp4_gemm_w4a4(self.axq, self.aw, out=self.ay)
+        mark("attn_dequantize")
+        nv.nvfp4_dequantize(self.axq, out=self.adq)
+        mark("ffn_quantize")
+        nv.nvfp4_quantize(self.fx, out=self.fxq, workspace=self.fws)
+        mark("ffn_gemm1")
+        self.famax.zero_()
+        nv.nvfp4_gemm_w4a4(self.fxq, self.fw1, out=self.fy1, y_amax=self.famax)
+        mark("ffn_requantize")
+        nv.nvfp4_quantize(self.fy1, out=self.fy1q, amax=self.famax)
+        mark("ffn_gemm2")
+        nv.nvfp4_gemm_w4a4(self.fy1q, self.fw2, out=self.fy2)
+        mark("kv_write")
+        nv.nvfp4_kv_quantize(self.kv_w, 0, 0, self.kv_k, self.kv_v, 0, workspace=self.kv_ws)
+        mark("kv_read")
+        for layer in range(self.lc_layers):
+            nv.nvfp4_kv_dequant_blocks(self.lc, layer, self.window, self.kh, self.vh)
+        mark(None)
+
+
+def run_gpu(steps, warmup):
+    import torch
+    dev = torch.device("cuda", 0)
+    wl = Workload(dev)
+    for _ in range(warmup):
+        wl.step()
+    torch.cuda.synchronize()
+
+    # whole-step wall time over exactly `steps` steps
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        wl.step()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+
+    # per-op durations from events on the launch stream (a separate, equal pass)
+    names = list(op_table())
+    acc = {n: 0.0 for n in names}
+    for _ in range(steps):
+        evs = []
+
+        def ev(name, evs=evs):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            evs.append((name, e))
+        wl.step(ev)
+        torch.cuda.synchronize()
+        for (n, a), (_, b) in zip(evs[:-1], evs[1:]):
+            acc[n] += a.elapsed_time(b) * 1e-3
+    per_op = {n: acc[n] / steps for n in names}
+    return wall, per_op
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+
+def cpu_baseline(ops):
+    """Time the oracle on a bounded sample of every op; extrapolate a step."""
+    import synth
+    from oracle import formats as F
+    from oracle import kvcache as KV
+    from oracle import nvfp4 as Q
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+
+    a = synth.attn_proj()
+    x = F.bf16_bits_to_f64(a["x"][:256])                  # 256 x 3072 activation rows
+    t = time.perf_counter()
+    xq = Q.quantize(x)
+    t_q = (time.perf_counter() - t) / x.size              # s per element
+    t = time.perf_counter()
+    Q.dequantize(xq, "bf16")
+    t_dq = (time.perf_counter() - t) / x.size
+    wq = Q.quantize(F.bf16_bits_to_f64(a["w"]))
+    xg = Q.NVFP4(xq.packed[:64], xq.scales[:64], xq.s_g)  # 64 x 3072 x 3072 product
+    t = time.perf_counter()
+    Q.gemm(xg, wq)
+    t_gemm = (time.perf_counter() - t) / (2 * 64 * 3072 * 3072)   # s per FLOP
+    kb, vb = synth.kv_chunk(t=1024)
+    pool = KV.KVPool(1, 24, 128, 256, 4, 1, np.arange(4)[None, :], 4)
+    t = time.perf_counter()
+    pool.write_chunk(0, 0, F.bf16_bits_to_f64(kb), F.bf16_bits_to_f64(vb), 0)
+    t_kvw = (time.perf_counter() - t) / kb.size           # per element of K (K and V done)
+    t = time.perf_counter()
+    pool.dequant_pages(0, [0, 1, 2, 3])
+    t_kvr = (time.perf_counter() - t) / 4                 # per page
+
+    est = {
+        "attn_quantize": t_q * 4096 * 3072,
+        "attn_gemm": t_gemm * ops["attn_gemm"]["flops"],
+        "attn_dequantize": t_dq * 4096 * 3072,
+        "ffn_quantize": t_q * 8192 * 3072,
+        "ffn_gemm1": t_gemm * ops["ffn_gemm1"]["flops"],
+        "ffn_requantize": t_q * 8192 * 14336,
+        "ffn_gemm2": t_gemm * ops["ffn_gemm2"]["flops"],
+        "kv_write": t_kvw * 7040 * 24 * 128,
+        "kv_read": t_kvr * 68 * 30,
+    }
+    step = sum(est.values())
+    roof = sum(roofline_seconds(o) for o in ops.values())
+    return {
+        "value": 100.0 * roof / step,
+        "unit": "% of MI355X roofline (whole step, extrapolated)",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": ("oracle timed on 256x3072 activation rows (quantize, bf16 dequantize), a "
+                   "64x3072x3072 exact GEMM, a 1024-token KV chunk write and 4 KV pages read; "
+                   "per-unit times scaled to the full step; elementwise numpy is single-"
+                   "threaded, the GEMM's fp64 BLAS uses the listed threads"),
+        "step_seconds_estimate": step,
+    }
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the hot path runs on one MI355X; see the sharding notes).", file=sys.stderr)
+        sys.exit(2)
+
+    ops = op_table()
+    wall, per_op = run_gpu(args.steps, args.warmup)
+    roof = sum(roofline_seconds(o) for o in ops.values())
+
+    per = {}
+    for n, o in ops.items():
+        s = per_op[n]
+        rec = {"ms": round(s * 1e3, 4), "roofline_frac": round(roofline_seconds(o) / s, 4)}
+        if "flops" in o:
+            rec["tflops"] = round(o["flops"] / s / 1e12, 2)
+        else:
+            rec["gbps"] = round(o["bytes"] / s / 1e9, 1)
+        if "compressed_bytes" in o:
+            rec["gbps_compressed_read"] = round(o["compressed_bytes"] / s / 1e9, 1)
+        per[n] = rec
+
+    g1 = per_op["ffn_gemm1"]
+    line = {
+        "metric": METRIC,
+        "value": round(100.0 * roof / wall, 3),
+        "unit": "% of MI355X roofline (whole step)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("DiT block hot path: attn proj quantize+GEMM 4096x3072x3072, dequantize, "
+                         "FFN pair 8192x3072->14336->3072 with requant, KV chunk write "
+                         "7040x24x128, KV window read 30 layers x 68 pages of 256 tokens"),
+            "roofline_seconds_per_step": roof,
+        },
+        "roofline": {
+            "kernel": "gemm_w4a4_kernel (FFN GEMM1 launch, M8192 N14336 K3072, bf16 out)",
+            "bound": "mfma",
+            "achieved": round(ops["ffn_gemm1"]["flops"] / g1 / 1e12, 2),
+            "peak": MFMA_BF16_FLOPS / 1e12,
+            "unit": "TFLOP/s",
+            "frac": round(ops["ffn_gemm1"]["flops"] / g1 / MFMA_BF16_FLOPS, 4),
+            "traffic": None,
+        },
+        "per_op": per,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(ops)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

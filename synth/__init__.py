@@ -152,6 +152,19 @@ class LongContextKV:
         zk, zv = self._base(c, t)
         return start, to_bf16_bits(zk + self.offset(layer)[None]), to_bf16_bits(zv)
 
+    def chunk_torch(self, layer, c, device):
+        """The same recipe drawn with torch's generator on ``device``: fast, but the
+        values differ from :meth:`chunk`.  For timing runs, where only the shapes
+        and the distribution matter."""
+        start, t = self.chunks[c]
+        g = torch.Generator(device=device)
+        g.manual_seed(1000 + 2 * c)
+        zk = torch.randn((t, self.H, self.D), generator=g, device=device)
+        g.manual_seed(1001 + 2 * c)
+        zv = torch.randn((t, self.H, self.D), generator=g, device=device)
+        off = torch.from_numpy(self.offset(layer)).to(device)
+        return start, (zk + off).to(torch.bfloat16), zv.to(torch.bfloat16)
+
     def window(self, sink_pages=4, recent_tokens=16384):
         """Logical pages of the attention window: sink pages + the most recent tokens."""
         last = self.pages_per_layer

@@ -238,12 +238,12 @@ void launch_gemm(const uint8_t* xc, const uint8_t* xs, bool x_tiled, const float
                  int64_t N, int64_t K, void* y, bool y_bf16, int64_t ld_y, float* y_amax,
                  hipStream_t stream) {
   const Operand xa{xc, xs, x_tiled}, wb{wc, ws, w_tiled};
-  // pick the tile width that leaves the fewest idle CUs in the last wave
+  // Pick the tile width with the shorter estimated run time: the number of
+  // waves of workgroups over the 256 CUs times the work of one tile.
   const int64_t nbm = (M + kBM - 1) / kBM;
   const int64_t t256 = nbm * ((N + 255) / 256), t192 = nbm * ((N + 191) / 192);
   auto waves = [](int64_t t) { return (t + 255) / 256; };
-  const bool use192 = waves(t192) < waves(t256) ||
-                      (waves(t192) == waves(t256) && t192 * 192 <= t256 * 256 && N % 256 != 0);
+  const bool use192 = waves(t192) * 192 < waves(t256) * 256;
   if (use192) {
     if (y_bf16) launch_bn<192, true>(xa, wb, xg, wg, M, N, K, y, ld_y, y_amax, stream);
     else launch_bn<192, false>(xa, wb, xg, wg, M, N, K, y, ld_y, y_amax, stream);
