@@ -294,111 +294,125 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(
 
 // ------------------------------------------------------------------ read: dequantize pages
 
-// Grid: x = listed page * slot tiles + slot tile, y = head.  Thread -> (slot, 64-value group).
-// The workgroup stages mu of the (at most two) chunks of its page and head in LDS.
-__global__ __launch_bounds__(256) void kv_dequant_kernel(KvGeom g, int64_t n_phys,
-                                                         const int32_t* __restrict__ pages,
+// Work unit = 8 consecutive values of one (token, head) row: one dword of codes
+// and half a scale byte in, 16 bytes of bf16 out, for K and for V.
+//
+// A workgroup covers `tt` tokens of one listed page and all heads.  Thread
+// `pos` owns the unit position (head h, value group sub) of a token row and
+// walks the tile's tokens, so its K mean (both chunks a page can hold) stays
+// in registers and the loop carries no index arithmetic beyond strides.  The
+// output of a token is one contiguous run of H * D bf16 values, unit pos at
+// bytes [16 pos, 16 pos + 16): consecutive lanes store consecutive 16 bytes.
+//
+// Exact rounding at low cost: V^ = RN_bf16(a s_gV) needs the midpoint fix-up
+// only for the rare s_gV that product_needs_check() flags (decided once per
+// chunk); for K^ = RN_bf16(a s_gK + mu) the eight fp32 FMA results of a unit
+// are tested together and the exact slow path runs only when one of them is
+// a bf16 midpoint.
+template <int kTok>
+__global__ __launch_bounds__(512) void kv_dequant_kernel(KvGeom g, int64_t n_phys,
+                                                         const int32_t* __restrict__ pages, int tt,
                                                          uint16_t* __restrict__ k_out,
                                                          uint16_t* __restrict__ v_out) {
   const int H = g.n_heads, D = g.head_dim, P = g.page_tokens;
-  const int gpr = (D + 63) / 64;
-  const int spw = 256 / gpr;                          // slots per workgroup
-  const int h = blockIdx.y;
-  const int tiles = (P + spw - 1) / spw;
+  const int upr = D / 8;                                  // units per (token, head) row
+  const int npos = H * upr;                               // units per token
+  const int tiles = (P + tt - 1) / tt;
   const int64_t i = blockIdx.x / tiles;
-  const int tile = blockIdx.x % tiles;
+  const int t0 = (blockIdx.x % tiles) * tt;
+  const int ntok = min(tt, P - t0);
   const int32_t lp = pages[i];
   bool valid = lp >= 0 && lp < g.max_pages;
-  int64_t phys = valid ? (int64_t)g.page_table[lp] : -1;
+  const int64_t phys = valid ? (int64_t)g.page_table[lp] : -1;
   valid = valid && phys >= 0 && phys < n_phys;
-  int c0 = 0, split = P;
-  if (valid) {
-    c0 = g.page_chunk[2 * lp];
-    split = g.page_chunk[2 * lp + 1];
-    c0 = c0 < 0 ? 0 : (c0 >= g.max_chunks ? g.max_chunks - 1 : c0);
-  }
-  const int c1 = c0 + 1 < g.max_chunks ? c0 + 1 : g.max_chunks - 1;
-  __shared__ float smu[2][256];
-  for (int j = threadIdx.x; j < 2 * D; j += 256) {
-    const int which = j / D, d = j % D;
-    smu[which][d] = g.k_mean[((int64_t)(which ? c1 : c0) * H + h) * D + d];
-  }
-  __syncthreads();
-  const int tid = threadIdx.x;
-  if (tid >= spw * gpr) return;
-  const int slot = tile * spw + tid / gpr;
-  const int grp = tid % gpr;
-  if (slot >= P) return;
-  const int64_t col0 = (int64_t)grp * 64;
-  const int left = (D - (int)col0) / 16;
-  const int nblk = left >= 4 ? 4 : left;
-  const int64_t orow = (i * P + slot) * H + h;       // output row (token, head)
-  uint16_t* ko = k_out + orow * D + col0;
-  uint16_t* vo = v_out + orow * D + col0;
+  const int64_t row_elems = (int64_t)H * D;               // bf16 values per output token
+  uint16_t* k_tile = k_out + (i * P + t0) * row_elems;
+  uint16_t* v_tile = v_out + (i * P + t0) * row_elems;
   if (!valid) {
-    for (int b = 0; b < nblk; ++b) {
-      *(u32x4*)(ko + 16 * b) = u32x4{0, 0, 0, 0};
-      *(u32x4*)(ko + 16 * b + 8) = u32x4{0, 0, 0, 0};
-      *(u32x4*)(vo + 16 * b) = u32x4{0, 0, 0, 0};
-      *(u32x4*)(vo + 16 * b + 8) = u32x4{0, 0, 0, 0};
+    for (int64_t u = threadIdx.x; u < (int64_t)ntok * npos; u += blockDim.x) {
+      *(u32x4*)(k_tile + 8 * u) = u32x4{0, 0, 0, 0};
+      *(u32x4*)(v_tile + 8 * u) = u32x4{0, 0, 0, 0};
     }
     return;
   }
-  const int which_c = slot < split ? 0 : 1;
-  const int c = which_c ? c1 : c0;
-  const float s_gk = g.k_gscale[c], s_gv = g.v_gscale[c];
-  const float* mu = &smu[which_c][col0];
+  int c0 = g.page_chunk[2 * lp];
+  const int split = g.page_chunk[2 * lp + 1];
+  c0 = c0 < 0 ? 0 : (c0 >= g.max_chunks ? g.max_chunks - 1 : c0);
+  const int c1 = c0 + 1 < g.max_chunks ? c0 + 1 : g.max_chunks - 1;
+  const float sgk0 = g.k_gscale[c0], sgk1 = g.k_gscale[c1];
+  const float sgv0 = g.v_gscale[c0], sgv1 = g.v_gscale[c1];
+  const bool vcheck = product_needs_check(sgv0) || product_needs_check(sgv1);
 
   const uint8_t* page = g.pool + phys * g.page_bytes;
-  const int64_t row = (int64_t)h * P + slot;
   const int64_t codes_region = (int64_t)H * P * (D / 2);
   const int64_t scales_region = (int64_t)H * P * (D / 16);
-  const uint8_t* kc = page + row * (D / 2) + grp * 32;
-  const uint8_t* ks = page + codes_region + row * (D / 16) + grp * 4;
-  const uint8_t* vc = page + codes_region + scales_region + row * (D / 2) + grp * 32;
-  const uint8_t* vs = page + 2 * codes_region + scales_region + row * (D / 16) + grp * 4;
 
-  for (int which = 0; which < 2; ++which) {
-    const uint8_t* cp = which == 0 ? kc : vc;
-    const uint8_t* sp = which == 0 ? ks : vs;
-    uint32_t sw;
-    if (nblk == 4 && (D % 64) == 0) {
-      sw = *(const uint32_t*)sp;
-    } else {
-      sw = 0;
-      for (int b = 0; b < nblk; ++b) sw |= (uint32_t)sp[b] << (8 * b);
+  for (int pos = threadIdx.x; pos < npos; pos += blockDim.x) {
+    const int h = pos / upr, sub = pos - (pos / upr) * upr;
+    float mu0[8], mu1[8];
+    {
+      const float* m0 = g.k_mean + ((int64_t)c0 * H + h) * D + 8 * sub;
+      const float* m1 = g.k_mean + ((int64_t)c1 * H + h) * D + 8 * sub;
+      const f32x4 a0 = *(const f32x4*)m0, a1 = *(const f32x4*)(m0 + 4);
+      const f32x4 b0 = *(const f32x4*)m1, b1 = *(const f32x4*)(m1 + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        mu0[j] = a0[j]; mu0[4 + j] = a1[j];
+        mu1[j] = b0[j]; mu1[4 + j] = b1[j];
+      }
     }
-    uint16_t* out = which == 0 ? ko : vo;
+    const int64_t r0 = (int64_t)h * P + t0;                // (head, slot) row of token t0
+    const uint8_t* kc = page + r0 * (D / 2) + 4 * sub;
+    const uint8_t* ks = page + codes_region + r0 * (D / 16) + (sub >> 1);
+    const uint8_t* vc = page + codes_region + scales_region + r0 * (D / 2) + 4 * sub;
+    const uint8_t* vs = page + 2 * codes_region + scales_region + r0 * (D / 16) + (sub >> 1);
+    for (int t = 0; t < ntok; t += kTok) {
+      uint32_t kcw[kTok], vcw[kTok], ksb[kTok], vsb[kTok];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      if (b < nblk) {
-        const u32x2 cw = *(const u32x2*)(cp + 8 * b);
-        const float s_b = e4m3_value((sw >> (8 * b)) & 0xFFu);
-        float o[16];
+      for (int j = 0; j < kTok; ++j) {
+        if (t + j < ntok) {
+          kcw[j] = *(const uint32_t*)(kc + (int64_t)(t + j) * (D / 2));
+          vcw[j] = *(const uint32_t*)(vc + (int64_t)(t + j) * (D / 2));
+          ksb[j] = ks[(int64_t)(t + j) * (D / 16)];
+          vsb[j] = vs[(int64_t)(t + j) * (D / 16)];
+        }
+      }
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
+      for (int j = 0; j < kTok; ++j) {
+        if (t + j < ntok) {
+          const bool second = t0 + t + j >= split;
+          const float sgk = second ? sgk1 : sgk0, sgv = second ? sgv1 : sgv0;
+          const float sbk = e4m3_value(ksb[j]), sbv = e4m3_value(vsb[j]);
+          float ka[8], kf[8], vf[8];
+          uint32_t off = 0xFFFFFFFFu;
 #pragma unroll
           for (int sel = 0; sel < 4; ++sel) {
-            const f32x2 q = e2m1_pair(cw[hh], sel);
-            const int e = 8 * hh + 2 * sel;
-            const float a0 = q[0] * s_b, a1 = q[1] * s_b;   // exact
-            if (which == 0) {
-              o[e] = fma_for_bf16(a0, s_gk, mu[16 * b + e]);
-              o[e + 1] = fma_for_bf16(a1, s_gk, mu[16 * b + e + 1]);
-            } else {
-              o[e] = mul_for_bf16(a0, s_gv);
-              o[e + 1] = mul_for_bf16(a1, s_gv);
+            const f32x2 qk = e2m1_pair(kcw[j], sel);
+            const f32x2 qv = e2m1_pair(vcw[j], sel);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int n = 2 * sel + e;
+              ka[n] = qk[e] * sbk;                          // exact
+              kf[n] = __builtin_fmaf(ka[n], sgk, second ? mu1[n] : mu0[n]);
+              off = min(off, off_midpoint(kf[n]));
+              vf[n] = vcheck ? mul_for_bf16(qv[e] * sbv, sgv) : (qv[e] * sbv) * sgv;
             }
           }
-        }
-        u32x4 p0, p1;
+          if (__builtin_expect(off == 0u, 0)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p0[j] = pack_bf16x2(o[2 * j], o[2 * j + 1]);
-          p1[j] = pack_bf16x2(o[8 + 2 * j], o[8 + 2 * j + 1]);
+            for (int n = 0; n < 8; ++n)
+              kf[n] = fma_for_bf16(ka[n], sgk, second ? mu1[n] : mu0[n]);
+          }
+          u32x4 ko, vo;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            ko[q] = pack_bf16x2(kf[2 * q], kf[2 * q + 1]);
+            vo[q] = pack_bf16x2(vf[2 * q], vf[2 * q + 1]);
+          }
+          const int64_t o = (int64_t)(t + j) * row_elems + 8 * pos;
+          *(u32x4*)(k_tile + o) = ko;
+          *(u32x4*)(v_tile + o) = vo;
         }
-        *(u32x4*)(out + 16 * b) = p0;
-        *(u32x4*)(out + 16 * b + 8) = p1;
       }
     }
   }
@@ -424,12 +438,14 @@ void launch_kv_quantize(const KvGeom& g, int32_t chunk_id, const uint16_t* k, co
 
 void launch_kv_dequant(const KvGeom& g, const int32_t* logical_pages, int32_t n_pages,
                        uint16_t* k_out, uint16_t* v_out, hipStream_t stream) {
-  const int gpr = (g.head_dim + 63) / 64;
-  const int spw = 256 / gpr;
-  const int64_t tiles = (g.page_tokens + spw - 1) / spw;
-  const dim3 grid((unsigned)(tiles * n_pages), (unsigned)g.n_heads);
-  hipLaunchKernelGGL(kv_dequant_kernel, grid, dim3(256), 0, stream, g, g.n_phys_pages,
-                     logical_pages, k_out, v_out);
+  // one thread per unit position of a token row (up to 512), 16 tokens per workgroup
+  const int npos = g.n_heads * (g.head_dim / 8);
+  int threads = ((npos + 63) / 64) * 64;
+  threads = threads > 512 ? 512 : threads;
+  const int tt = g.page_tokens < 16 ? g.page_tokens : 16;
+  const int64_t tiles = (g.page_tokens + tt - 1) / tt;
+  hipLaunchKernelGGL(kv_dequant_kernel<4>, dim3((unsigned)(tiles * n_pages)), dim3(threads), 0,
+                     stream, g, g.n_phys_pages, logical_pages, tt, k_out, v_out);
 }
 
 }  // namespace nvfp4

@@ -198,6 +198,29 @@ __device__ __forceinline__ float mul_for_bf16(float a, float g) {
   return p;
 }
 
+// Whether mul_for_bf16(a, g) can ever take its slow branch for this g, over
+// every decoded a = q s_b (q an E2M1 magnitude, s_b an E4M3 scale).  While
+// a g is a normal fp32 number, the low bits of RN32(a g) depend only on the
+// significands of a and g, and a's significand is one of the 16 products
+// {1, 1.5} x (1 + m/8); so testing those 16 values of a decides it for all.
+// g below 2^-116 (products that may be subnormal) always answers yes.
+__device__ __forceinline__ bool product_needs_check(float g) {
+  if (!(g >= 0x1p-116f)) return true;
+  bool need = false;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float a = ((i & 8) ? 1.5f : 1.0f) * (1.0f + (float)(i & 7) * 0.125f);
+    const float p = a * g;
+    need |= (__float_as_uint(p) & 0xFFFFu) == 0x8000u && __builtin_fmaf(a, g, -p) != 0.0f;
+  }
+  return need;
+}
+
+// Nonzero unless the fp32 number f is exactly a bf16 midpoint (low 16 bits 0x8000).
+__device__ __forceinline__ uint32_t off_midpoint(float f) {
+  return (__float_as_uint(f) & 0xFFFFu) ^ 0x8000u;
+}
+
 // RN_bf16(a * g + mu) with one rounding of the exact value.  f = RN32(a g + mu)
 // (one FMA) decides correctly unless it is exactly a bf16 midpoint; then the
 // exact value is compared with f in fp64: A = a g is exact in fp64 (30 bits),
