@@ -46,22 +46,36 @@ struct Operand {
   bool tiled;
 };
 
-// Byte offset of the scale dword (4 blocks of 16) of row r, K step ks.
-__device__ __forceinline__ int64_t scale_dword_offset(int64_t r, int ks, int64_t K, bool tiled) {
-  return tiled ? ((r >> 7) * (K / 64) + ks) * 512 + (r & 127) * 4 : r * (K / 16) + ks * 4;
-}
-
 struct Slice {
   u32x4 c0, c1;      // 64 codes
   uint32_t s;        // 4 scale bytes
 };
 
-__device__ __forceinline__ Slice fetch(const Operand& o, int64_t r, int ks, int64_t K) {
+// Per-thread source of one operand row: K step ks reads 32 bytes of codes at
+// codes + 32 ks and the scale dword (blocks 4 ks .. 4 ks + 3) at
+// scales + ks * sstride.  In the row-major layout the dword follows the
+// previous one (stride 4); in the 128-row tiled layout the next 64 columns
+// of the same row are one 512-byte tile further on (stride 512).
+struct RowSrc {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int sstride;
+};
+
+__device__ __forceinline__ RowSrc row_src(const Operand& o, int64_t r, int64_t K) {
+  RowSrc rs;
+  rs.codes = o.codes + r * (K / 2);
+  rs.scales = o.scales + (o.tiled ? (r >> 7) * (K / 64) * 512 + (r & 127) * 4 : r * (K / 16));
+  rs.sstride = o.tiled ? 512 : 4;
+  return rs;
+}
+
+__device__ __forceinline__ Slice fetch(const RowSrc& rs, int ks) {
   Slice sl;
-  const uint8_t* cp = o.codes + r * (K / 2) + ks * 32;
+  const uint8_t* cp = rs.codes + ks * 32;
   sl.c0 = *(const u32x4*)cp;
   sl.c1 = *(const u32x4*)(cp + 16);
-  sl.s = *(const uint32_t*)(o.scales + scale_dword_offset(r, ks, K, o.tiled));
+  sl.s = *(const uint32_t*)(rs.scales + (int64_t)ks * rs.sstride);
   return sl;
 }
 
@@ -111,6 +125,123 @@ __device__ __forceinline__ void tile_of(int bid, int nbm, int nbn, int& tm, int&
   tn = in / rows;
 }
 
+// Decode blocks [b0, b0 + 2) of a slice (32 values) into an LDS row.
+__device__ __forceinline__ void decode_half(const Slice& sl, int half, uint16_t* __restrict__ row) {
+  const uint32_t cw[8] = {sl.c0[0], sl.c0[1], sl.c0[2], sl.c0[3],
+                          sl.c1[0], sl.c1[1], sl.c1[2], sl.c1[3]};
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    const int b = 2 * half + bb;
+    const float s_b = e4m3_value((sl.s >> (8 * b)) & 0xFFu);
+    uint32_t o[8];
+    decode8(cw[2 * b], s_b, o);
+    decode8(cw[2 * b + 1], s_b, o + 4);
+    *(u32x4*)(row + 16 * b) = u32x4{o[0], o[1], o[2], o[3]};
+    *(u32x4*)(row + 16 * b + 8) = u32x4{o[4], o[5], o[6], o[7]};
+  }
+}
+
+template <int TM, int TN, int WN>
+struct Frags {
+  bf16x8 a[TM], b[TN];
+};
+
+template <int TM, int TN, int WN>
+__device__ __forceinline__ void load_frags(Frags<TM, TN, WN>& f, const uint16_t* __restrict__ As,
+                                           const uint16_t* __restrict__ Bs, int kk, int lane,
+                                           int wm, int wn) {
+  const int kc = kk * 16 + (lane >> 5) * 8;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+    f.a[i] = *(const bf16x8*)(As + (wm * 128 + i * 32 + (lane & 31)) * kLdsRow + kc);
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+    f.b[j] = *(const bf16x8*)(Bs + (wn * WN + j * 32 + (lane & 31)) * kLdsRow + kc);
+}
+
+// One K step, software-pipelined, with an explicit instruction order.
+//
+// On entry `f0` holds the fragments of k16 sub-step 0 of stage As/Bs.  The
+// step issues TM*TN*4 MFMAs.  Between consecutive MFMAs it places a slice of
+// the decode of the next step (16 units: the 8 code dwords of the X slice and
+// the 8 of the W slice, each 4 x {fp4->fp32 pair, 2 exact multiplies, bf16
+// pack} plus one 16-byte LDS store into stage An), and during the first MFMAs
+// of sub-step kk the fragment loads of kk+1.  Scheduling fences keep that
+// order: an MFMA occupies the matrix pipe for 32 cycles, and the VALU work that
+// follows it in program order issues underneath instead of queueing behind the
+// next MFMA.  The stage pointers are restrict-qualified (the stages never
+// overlap), so stores to An may pass loads from As/Bs.
+template <int TM, int TN, int WN>
+__device__ __forceinline__ void gemm_step(f32x16 (&acc)[TM][TN], Frags<TM, TN, WN>& f0,
+                                          Frags<TM, TN, WN>& f1,
+                                          const uint16_t* __restrict__ As,
+                                          const uint16_t* __restrict__ Bs,
+                                          uint16_t* __restrict__ An, const Slice& ca,
+                                          const Slice& cb, int tid, int lane, int wm, int wn) {
+  constexpr int kSub = kBK / 16;
+  constexpr int kPer = TM * TN;                    // MFMAs per sub-step
+  constexpr int kTotal = kPer * kSub;              // MFMAs per step
+  constexpr int kUnits = 16;                       // decode units per step
+  static_assert(kTotal % kUnits == 0, "MFMA count must split evenly over the decode units");
+  constexpr int kMpu = kTotal / kUnits;            // MFMAs per decode unit (4 or 3)
+
+  const uint32_t cw[16] = {ca.c0[0], ca.c0[1], ca.c0[2], ca.c0[3], ca.c1[0], ca.c1[1],
+                           ca.c1[2], ca.c1[3], cb.c0[0], cb.c0[1], cb.c0[2], cb.c0[3],
+                           cb.c1[0], cb.c1[1], cb.c1[2], cb.c1[3]};
+  float sc[8];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    sc[b] = e4m3_value((ca.s >> (8 * b)) & 0xFFu);
+    sc[4 + b] = e4m3_value((cb.s >> (8 * b)) & 0xFFu);
+  }
+  uint16_t* rowA = An + tid * kLdsRow;
+  uint16_t* rowB = An + (kBM + tid) * kLdsRow;
+  uint32_t out[4];
+  __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+  for (int kk = 0; kk < kSub; ++kk) {
+    Frags<TM, TN, WN>& cur = (kk & 1) ? f1 : f0;
+    Frags<TM, TN, WN>& nxt = (kk & 1) ? f0 : f1;
+    const int kc = (kk + 1) * 16 + (lane >> 5) * 8;
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      const int i = kk * kPer + m;                 // MFMA index within the step
+      // fragment load for sub-step kk+1 (one per MFMA until all are issued)
+      if (kk + 1 < kSub && m < TM + TN) {
+        if (m < TM)
+          nxt.a[m] = *(const bf16x8*)(As + (wm * 128 + m * 32 + (lane & 31)) * kLdsRow + kc);
+        else
+          nxt.b[m - TM] =
+              *(const bf16x8*)(Bs + (wn * WN + (m - TM) * 32 + (lane & 31)) * kLdsRow + kc);
+      }
+      acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          cur.a[m / TN], cur.b[m % TN], acc[m / TN][m % TN], 0, 0, 0);
+      // decode slice: unit u, part p of kMpu; the 4 selectors of the unit's code
+      // dword are split over the parts
+      const int u = i / kMpu, p = i % kMpu;
+      const int sel0 = p * 4 / kMpu, sel1 = (p + 1) * 4 / kMpu;
+#pragma unroll
+      for (int sel = 0; sel < 4; ++sel) {
+        if (sel >= sel0 && sel < sel1) {
+          const float s_b = sc[(u >> 3) * 4 + ((u & 7) >> 1)];
+          const f32x2 q = sel == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u], 1.0f, 0)
+                        : sel == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u], 1.0f, 1)
+                        : sel == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u], 1.0f, 2)
+                                   : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u], 1.0f, 3);
+          const uint32_t lo = __float_as_uint(q[0] * s_b), hi = __float_as_uint(q[1] * s_b);
+          out[sel] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+        }
+      }
+      if (p == kMpu - 1) {
+        uint16_t* row = (u < 8) ? rowA : rowB;
+        *(u32x4*)(row + 8 * (u & 7)) = u32x4{out[0], out[1], out[2], out[3]};
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 }  // namespace
 
 template <int BN, bool kOutBf16>
@@ -120,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_kernel(
     int nbn) {
   constexpr int WN = BN / 2;                // wave tile 128 x WN
   constexpr int TM = 4, TN = WN / 32;
-  constexpr int kStage = (kBM + BN) * kLdsRow;   // bf16 per LDS stage
+  constexpr int kStage = 2 * kBM * kLdsRow;  // bf16 per LDS stage: 256 A rows + 256 B rows
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
   int tm, tn;
@@ -129,10 +260,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const int nk = (int)(K / kBK);
 
-  // loader rows (clamped into range; results of clamped rows are never stored)
-  const int64_t ar = min((int64_t)tm * kBM + tid, (int64_t)M - 1);
-  const bool has_b = tid < BN;
-  const int64_t br = min((int64_t)tn * BN + (has_b ? tid : 0), (int64_t)N - 1);
+  // Loader rows, clamped into range (results of clamped rows are never
+  // stored).  With BN < 256 the spare threads load a valid W row and write it
+  // to LDS rows the MFMAs never read, which keeps the main loop branch-free.
+  const RowSrc ra = row_src(xa, min((int64_t)tm * kBM + tid, (int64_t)M - 1), K);
+  const RowSrc rb = row_src(wb, min((int64_t)tn * BN + (tid < BN ? tid : BN - 1), (int64_t)N - 1), K);
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -142,48 +274,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  // Pipeline: step s computes on LDS stage s&1, decodes the slices of step
+  // s+1 (fetched during step s-1) into the other stage, and issues the global
+  // loads of step s+2.  The decode (VALU + LDS stores) and the MFMAs of a step
+  // are independent, so they form one basic block that the scheduler
+  // interleaves; one barrier per step.
   {
-    const Slice a = fetch(xa, ar, 0, K);
-    decode_to_lds(a, lds + tid * kLdsRow);
-    if (has_b) {
-      const Slice b = fetch(wb, br, 0, K);
-      decode_to_lds(b, lds + (kBM + tid) * kLdsRow);
-    }
+    const Slice a0 = fetch(ra, 0), b0 = fetch(rb, 0);
+    decode_to_lds(a0, lds + tid * kLdsRow);
+    decode_to_lds(b0, lds + (kBM + tid) * kLdsRow);
   }
+  Slice ca = fetch(ra, nk > 1 ? 1 : 0), cb = fetch(rb, nk > 1 ? 1 : 0);
   __syncthreads();
+  Frags<TM, TN, WN> f0, f1;
+  load_frags(f0, lds, lds + kBM * kLdsRow, 0, lane, wm, wn);
 
   for (int s = 0; s < nk; ++s) {
     const int cur = s & 1;
-    const bool more = s + 1 < nk;
-    Slice na, nb;
-    if (more) {
-      na = fetch(xa, ar, s + 1, K);
-      if (has_b) nb = fetch(wb, br, s + 1, K);
-    }
+    const int s2 = s + 2 < nk ? s + 2 : nk - 1;
+    const Slice na = fetch(ra, s2), nb = fetch(rb, s2);
     const uint16_t* As = lds + cur * kStage;
-    const uint16_t* Bs = As + kBM * kLdsRow;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int kc = kk * 16 + (lane >> 5) * 8;
-      bf16x8 af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *(const bf16x8*)(As + (wm * 128 + i * 32 + (lane & 31)) * kLdsRow + kc);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *(const bf16x8*)(Bs + (wn * WN + j * 32 + (lane & 31)) * kLdsRow + kc);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      uint16_t* An = lds + (cur ^ 1) * kStage;
-      decode_to_lds(na, An + tid * kLdsRow);
-      if (has_b) decode_to_lds(nb, An + (kBM + tid) * kLdsRow);
-    }
+    uint16_t* An = lds + (cur ^ 1) * kStage;
+    gemm_step<TM, TN, WN>(acc, f0, f1, As, As + kBM * kLdsRow, An, ca, cb, tid, lane, wm, wn);
     __syncthreads();
+    load_frags(f0, An, An + kBM * kLdsRow, 0, lane, wm, wn);   // sub-step 0 of the next step
+    ca = na;
+    cb = nb;
   }
 
   // epilogue: Y = acc * (s_gx s_gw), rounded once to the output type
@@ -222,7 +338,7 @@ static void launch_bn(const Operand& xa, const Operand& wb, const float* xg, con
                       int64_t M, int64_t N, int64_t K, void* y, int64_t ld_y, float* y_amax,
                       hipStream_t stream) {
   const int nbm = (int)((M + kBM - 1) / kBM), nbn = (int)((N + BN - 1) / BN);
-  const size_t lds = 2 * (size_t)(kBM + BN) * kLdsRow * sizeof(uint16_t);
+  const size_t lds = 2 * (size_t)(2 * kBM) * kLdsRow * sizeof(uint16_t);
   auto kern = gemm_w4a4_kernel<BN, kOutBf16>;
   // raise the dynamic-LDS limit once per instantiation (thread-safe static init)
   static const bool configured =

@@ -38,11 +38,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // ------------------------------------------------------------------ scales
 
 // Value of an E4M3FN byte in 0x00..0x7E (bias 7; exponent field 0 is m/8 * 2^-6).
+// gfx950's fp8 -> fp32 conversion uses the OCP E4M3FN encoding; it was checked
+// on the device against the bit definition for all 127 finite non-negative
+// bytes, and the dequantize parity tests cover every scale byte.
 __device__ __forceinline__ float e4m3_value(uint32_t b) {
-  uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  float normal = __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1 + m/8) 2^(e-7)
-  float sub = (float)m * 0x1p-9f;                                   // m 2^-9
-  return e ? normal : sub;
+  return __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
 }
 
 // s_g = RN32(amax / 2688), or 1 when amax == 0.  __fdiv_rn is the correctly
