@@ -66,8 +66,9 @@ typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype_t;
 
 typedef enum { NVFP4_SCALES_ROWMAJOR = 0, NVFP4_SCALES_TILED = 1 } nvfp4_scale_layout_t;
 
-/* An NVFP4 tensor [rows x cols] (cols % 16 == 0).  The struct itself is a
- * host object; its pointers are device pointers. */
+/* An NVFP4 tensor [rows x cols] (cols % 16 == 0, cols <= 65535 * 128,
+ * rows <= 2^37; larger sizes give ESHAPE).  The struct itself is a host
+ * object; its pointers are device pointers. */
 typedef struct {
   uint8_t* codes;        /* rows * cols / 2 bytes                               */
   uint8_t* scales;       /* rows * cols / 16 bytes, in `scale_layout`           */

@@ -21,12 +21,17 @@ inline int finish() {
 
 inline hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
+// quantize/dequantize grids: one workgroup per 128 x 128 tile, columns on grid.y
+constexpr int64_t kMaxCols = int64_t(65535) * 128;
+constexpr int64_t kMaxRows = int64_t(1) << 37;
+
 int check_tensor(const nvfp4_tensor_t* t) {
   if (!t) return NVFP4_EINVAL;
   if (t->rows < 0 || t->cols < 0) return NVFP4_EINVAL;
   if (t->scale_layout != NVFP4_SCALES_ROWMAJOR && t->scale_layout != NVFP4_SCALES_TILED)
     return NVFP4_EINVAL;
   if (t->cols % 16) return NVFP4_ESHAPE;
+  if (t->cols > kMaxCols || t->rows > kMaxRows) return NVFP4_ESHAPE;
   if (!t->global_scale) return NVFP4_EINVAL;
   if (t->rows > 0 && t->cols > 0 && (!t->codes || !t->scales)) return NVFP4_EINVAL;
   if (t->scale_layout == NVFP4_SCALES_TILED && (t->rows % 128 || t->cols % 64))

@@ -199,6 +199,7 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(
     KvGeom g, int64_t n_phys, const float* __restrict__ mu_chunk) {
   const float s_gk = global_scale(max_of(ws.kamax, n_fin_wg));
   const float s_gv = global_scale(max_of(ws.vamax, n_stats_wg));
+  const TensorEnc tk = make_tensor_enc(s_gk), tv = make_tensor_enc(s_gv);
   const int H = g.n_heads, D = g.head_dim, P = g.page_tokens;
   const int gpr = (D + 63) / 64;                     // 64-value groups per (token, head)
   const int tpw = 256 / gpr;                         // tokens per workgroup
@@ -258,7 +259,6 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(
         }
       }
     }
-    const float s_g = which == 0 ? s_gk : s_gv;
     if (which == 0) {
       const float* mu = mu_chunk + (int64_t)h * D + col0;
 #pragma unroll
@@ -275,9 +275,7 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(
     }
     uint32_t cw[8];
     uint32_t sw;
-    const double six_sg = 6.0 * (double)s_g;
-    if (s_g < 0x1p-100f) quantize_group<true>(x, nblk, s_g, six_sg, cw, sw);
-    else quantize_group<false>(x, nblk, s_g, six_sg, cw, sw);
+    quantize_group(x, nblk, which == 0 ? tk : tv, cw, sw);
     uint8_t* cp = which == 0 ? kc : vc;
     uint8_t* sp = which == 0 ? ks : vs;
     // rows of codes are head_dim/2 bytes: 8-byte aligned for any head_dim % 16 == 0

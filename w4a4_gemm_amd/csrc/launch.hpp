@@ -10,7 +10,7 @@
 namespace nvfp4 {
 
 // ---- quantize / dequantize (quant.hip)
-constexpr int kAmaxPartials = 1024;   // max partial maxima written by the amax pass
+constexpr int kAmaxPartials = 1024;   // partial maxima written by the amax pass (multiple of 256)
 
 // Workspace floats used by the amax pass (partials), 256-byte rounded.
 size_t quantize_workspace_bytes(int64_t rows, int64_t cols, bool has_amax);

@@ -70,48 +70,73 @@ __device__ __forceinline__ uint32_t e4m3_block_scale(float b, double six_sg) {
   return (uint32_t)(bits >> 49) - ((1023u - 7u) << 3);  // rebias exponent 1023 -> 7
 }
 
-// ------------------------------------------------------------------ E2M1 encoding
+// ------------------------------------------------------------------ encoding
 
-// Per-block encoder state.  Codes come from the hardware fp32 -> E2M1
-// conversion (RNE, saturating at 6, sign kept; checked exhaustively against
-// the exact rule) applied to y = x * c for two multipliers that bracket the
-// exact 1 / (s_b s_g) from below and above:
-//   c_lo = RN32(inv (1 - 2^-20)),  c_hi = RN32(inv (1 + 2^-20)),  inv = RN64(1 / (s_b s_g))
-// so |x| c_lo (1 + 2^-24) < r < |x| c_hi (1 - 2^-24) with r = |x| / (s_b s_g).
-// The conversion is monotone, so equal codes for both are the code of r.
-// Where they differ (r within 2^-20 of an E2M1 midpoint M, or exactly on it)
-// the exact comparison  |x| - M s_b s_g  decides: M s_b has at most 7 bits, so
-// one fp32 FMA gives that difference with a single rounding and an exact sign.
-//
-// `pre` (1 or 2^64) scales x up for tensors with s_g < 2^-100 so that c stays
-// inside the fp32 range; the scaling is exact and cancels in the codes.
-struct BlockEnc {
-  float c_lo, c_hi;   // multipliers (0 when s_b == 0: every code is sign | 0)
-  float msb_neg[7];   // -(M_k s_b) for the 7 E2M1 midpoints
-  float sg_pre;       // s_g * pre
+// Per-tensor encoder constants.
+//   pre    1, or 2^64 when s_g < 2^-100: x is scaled up exactly so that the
+//          reciprocals below stay inside the fp32 range; it cancels in the codes.
+//   i6_lo, i6_hi  RN32(r (1 -/+ 2^-19)) with r = RN64(1 / (6 s_g)): they bracket
+//          1 / (6 s_g) from below and above by more than their rounding error.
+struct TensorEnc {
+  float s_g, pre, i6_lo, i6_hi;
+  double six_sg;                            // 6 s_g, exact in fp64
 };
 
-__device__ __forceinline__ BlockEnc make_block_enc(uint32_t sb_byte, float s_b, float s_g,
-                                                   float pre) {
+__device__ __forceinline__ TensorEnc make_tensor_enc(float s_g) {
+  TensorEnc t;
+  t.s_g = s_g;
+  t.pre = s_g < 0x1p-100f ? 0x1p64f : 1.0f;
+  t.six_sg = 6.0 * (double)s_g;
+  const double r = 1.0 / t.six_sg;
+  t.i6_lo = (float)(r * (1.0 - 0x1p-19));
+  t.i6_hi = (float)(r * (1.0 + 0x1p-19));
+  return t;
+}
+
+// Block scale byte = E4M3 value nearest to t = b / (6 s_g).  b i6_lo < t <
+// b i6_hi (each product within 2^-24 of its exact value, the bracket 2^-19
+// wide).  gfx950's fp32 -> E4M3 conversion is RNE (checked on the device
+// against the exact rule for every fp32 in [0, 448]) and monotone, so equal
+// bytes for both ends are the byte of t; otherwise t lies within 2^-19 of an
+// E4M3 midpoint, or on one, and the exact fp64 path decides.  Clamping at 448
+// is exact: with saturation every t >= 448 gives 448.  Products below the
+// fp32 normal range are far below 2^-10 and give byte 0 either way.
+__device__ __forceinline__ uint32_t block_scale_byte(float b, const TensorEnc& t) {
+  const float tl = fminf(b * t.i6_lo, 448.0f), th = fminf(b * t.i6_hi, 448.0f);
+  const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(tl, th, 0, false);
+  const uint32_t lo = pk & 0xFFu, hi = (pk >> 8) & 0xFFu;
+  if (__builtin_expect(lo == hi, 1)) return lo;
+  return e4m3_block_scale(b, t.six_sg);
+}
+
+// Per-block encoder.  Codes come from gfx950's fp32 -> E2M1 conversion (RNE,
+// saturating at 6, sign kept; checked on the device against the exact rule
+// for every fp32 with |x| <= 8) applied to y = x c for two multipliers that
+// bracket R = 1 / (s_b s_g pre):  p = RN32(s_b s_g pre) (relative error <=
+// 2^-24), r = rcp(p) (<= 1 ulp), c = RN32(r (1 -/+ 2^-19)); hence
+//   |x| c_lo (1 + 2^-24) < |x| R < |x| c_hi (1 - 2^-24).
+// The conversion is monotone, so equal codes for both are the code of |x| R.
+// Where they differ (|x| R within about 2^-19 of an E2M1 midpoint M, or on it)
+// the exact comparison |x| - M s_b s_g decides: M s_b has at most 7 bits, so
+// one fp32 FMA gives that difference with a single rounding and an exact sign.
+struct BlockEnc {
+  float c_lo, c_hi;   // 0 when s_b == 0: every code is then sign | 0
+  float s_b;
+};
+
+__device__ __forceinline__ BlockEnc make_block_enc(uint32_t sb_byte, const TensorEnc& t) {
   BlockEnc e;
-  if (sb_byte == 0) {
-    e.c_lo = 0.0f;
-    e.c_hi = 0.0f;
-  } else {
-    double inv = 1.0 / ((double)s_b * (double)s_g * (double)pre);   // product exact in fp64
-    e.c_lo = (float)(inv * (1.0 - 0x1p-20));
-    e.c_hi = (float)(inv * (1.0 + 0x1p-20));
-  }
-  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
-#pragma unroll
-  for (int k = 0; k < 7; ++k) e.msb_neg[k] = -(mids[k] * s_b);
-  e.sg_pre = s_g * pre;
+  e.s_b = e4m3_value(sb_byte);
+  const float r = __builtin_amdgcn_rcpf(e.s_b * (t.s_g * t.pre));
+  e.c_lo = sb_byte ? r * (1.0f - 0x1p-19f) : 0.0f;
+  e.c_hi = sb_byte ? r * (1.0f + 0x1p-19f) : 0.0f;
   return e;
 }
 
 // Codes of 8 values (x already multiplied by `pre`) -> 8 nibbles, value j in
 // bits 4j+3..4j (so byte i holds values 2i, 2i+1 with the even one low).
-__device__ __forceinline__ uint32_t encode8(const float* x, const BlockEnc& e) {
+__device__ __forceinline__ uint32_t encode8(const float* x, const BlockEnc& e,
+                                            const TensorEnc& t) {
   uint32_t lo = 0, hi = 0;
   lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x[0] * e.c_lo, x[1] * e.c_lo, 1.0f, 0);
   hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[0] * e.c_hi, x[1] * e.c_hi, 1.0f, 0);
@@ -123,18 +148,17 @@ __device__ __forceinline__ uint32_t encode8(const float* x, const BlockEnc& e) {
   hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[6] * e.c_hi, x[7] * e.c_hi, 1.0f, 3);
   if (__builtin_expect(lo != hi, 0)) {
     // resolve each differing nibble exactly
+    const float sg_pre = t.s_g * t.pre;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      uint32_t cl = (lo >> (4 * j)) & 0xFu, ch = (hi >> (4 * j)) & 0xFu;
+      const uint32_t cl = (lo >> (4 * j)) & 0xFu, ch = (hi >> (4 * j)) & 0xFu;
       if (cl != ch) {
-        uint32_t ml = cl & 7u;                          // magnitudes ml and ml + 1
-        float nms = e.msb_neg[0];
-#pragma unroll
-        for (int k = 1; k < 7; ++k) nms = (ml == (uint32_t)k) ? e.msb_neg[k] : nms;
-        float d = __builtin_fmaf(nms, e.sg_pre, __builtin_fabsf(x[j]));   // sign exact
-        bool up = d > 0.0f || (d == 0.0f && (ml & 1u));  // tie: to the even magnitude
-        uint32_t c = up ? ch : cl;
-        lo = (lo & ~(0xFu << (4 * j))) | (c << (4 * j));
+        const uint32_t ml = cl & 7u;                     // magnitudes ml and ml + 1
+        const float mid = ml == 0 ? 0.25f : ml == 1 ? 0.75f : ml == 2 ? 1.25f
+                        : ml == 3 ? 1.75f : ml == 4 ? 2.5f : ml == 5 ? 3.5f : 5.0f;
+        const float d = __builtin_fmaf(-(mid * e.s_b), sg_pre, __builtin_fabsf(x[j]));
+        const bool up = d > 0.0f || (d == 0.0f && (ml & 1u));   // tie: to the even magnitude
+        lo = (lo & ~(0xFu << (4 * j))) | ((up ? ch : cl) << (4 * j));
       }
     }
   }
@@ -145,9 +169,8 @@ __device__ __forceinline__ uint32_t encode8(const float* x, const BlockEnc& e) {
 
 // Quantize `nblk` (1..4) blocks held in v[0 .. 16*nblk) into codes and scale bytes.
 template <bool kPre>
-__device__ __forceinline__ void quantize_group(float* v, int nblk, float s_g, double six_sg,
+__device__ __forceinline__ void quantize_group(float* v, int nblk, const TensorEnc& t,
                                                uint32_t* code_words, uint32_t& scale_word) {
-  const float pre = kPre ? 0x1p64f : 1.0f;
   scale_word = 0;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -155,17 +178,24 @@ __device__ __forceinline__ void quantize_group(float* v, int nblk, float s_g, do
       float bm = 0.0f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) bm = fmaxf(bm, __builtin_fabsf(v[16 * b + j]));
-      const uint32_t sb = e4m3_block_scale(bm, six_sg);
-      const BlockEnc enc = make_block_enc(sb, e4m3_value(sb), s_g, pre);
+      const uint32_t sb = block_scale_byte(bm, t);
+      const BlockEnc enc = make_block_enc(sb, t);
       if (kPre) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) v[16 * b + j] *= pre;
+        for (int j = 0; j < 16; ++j) v[16 * b + j] *= 0x1p64f;
       }
-      code_words[2 * b] = encode8(v + 16 * b, enc);
-      code_words[2 * b + 1] = encode8(v + 16 * b + 8, enc);
+      code_words[2 * b] = encode8(v + 16 * b, enc, t);
+      code_words[2 * b + 1] = encode8(v + 16 * b + 8, enc, t);
       scale_word |= sb << (8 * b);
     }
   }
+}
+
+// Dispatch on the (tensor-uniform) pre-scaling.
+__device__ __forceinline__ void quantize_group(float* v, int nblk, const TensorEnc& t,
+                                               uint32_t* code_words, uint32_t& scale_word) {
+  if (t.pre != 1.0f) quantize_group<true>(v, nblk, t, code_words, scale_word);
+  else quantize_group<false>(v, nblk, t, code_words, scale_word);
 }
 
 // ------------------------------------------------------------------ decoding
@@ -245,6 +275,19 @@ __device__ __forceinline__ float fma_for_bf16(float a, float g, float mu) {
 }
 
 // ------------------------------------------------------------------ reductions
+
+// max(v, v of lane ^ 1): the two lanes of a 16-value block (DPP quad_perm 1,0,3,2).
+__device__ __forceinline__ float pair_max(float v) {
+  const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false);
+  return fmaxf(v, __int_as_float(o));
+}
+
+// Lanes l, l+2, l+4, l+6 each hold one scale byte `sb`; lane l (l % 8 == 0)
+// receives them as one little-endian word.  Every lane must execute it.
+__device__ __forceinline__ uint32_t gather_scale_word(uint32_t sb) {
+  const uint32_t w2 = sb | ((uint32_t)__shfl_down((int)sb, 2, 64) << 8);
+  return w2 | ((uint32_t)__shfl_down((int)w2, 4, 64) << 16);
+}
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -7,49 +7,68 @@
 // the E2M1 codes in registers (the fused scale+quantize kernel the
 // ai-manual.ru article credits with a 20% saving).
 //
-// Layout of work: a workgroup is 4 waves; lane l of wave w handles row
-// (64 * blockIdx.x + l) and the 64-column group (4 * blockIdx.y + w), i.e.
-// four blocks.  Each lane reads one 128-byte (bf16) or 256-byte (fp32) run with
-// 16-byte loads, writes 32 bytes of codes and one dword of scale bytes; in
-// the tiled scale layout the 64 lanes' dwords are contiguous.
+// Layout of work (quantize and dequantize): a workgroup covers a tile of 128
+// rows x 128 columns.  Lane l of wave w owns 8 consecutive values, column
+// chunk j = l % 16 of the tile, in rows 32 w + 4 t + l / 16 for t = 0..7.  A
+// wave's load instruction therefore reads 4 rows x 256 contiguous bytes (bf16),
+// two neighbouring lanes form one 16-value block (the even one stores its
+// scale byte), a lane's 8 codes are one dword (16 lanes store a row's 64
+// contiguous bytes), and the workgroup writes both 512-byte tiles of the tiled
+// scale layout that its 128 rows touch.
 
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
 namespace nvfp4 {
 
+namespace {
+constexpr int kTile = 128;         // tile rows and columns
+constexpr int kTasks = 8;          // rows per lane
+constexpr int kAmaxUnroll = 8;     // 16-byte loads in flight per lane in the amax pass
+}  // namespace
+
 // ------------------------------------------------------------------ amax pass
 
+__device__ __forceinline__ uint32_t fold_abs_bits(uint32_t m, const u32x4 w, bool bf16) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (bf16) {
+      const uint32_t a = w[j] & 0x7FFF7FFFu;
+      m = max(m, max(a & 0xFFFFu, a >> 16));
+    } else {
+      m = max(m, w[j] & 0x7FFFFFFFu);
+    }
+  }
+  return m;
+}
+
+// Partial max|x| per workgroup, as fp32.  The max of |x| bit patterns is the
+// bit pattern of max|x| (finite inputs).  Dense tensors are walked as one flat
+// array of 16-byte chunks, consecutive lanes on consecutive chunks; strided
+// ones row by row.
 template <bool kBf16>
 __global__ __launch_bounds__(256) void amax_partial_kernel(const void* __restrict__ xv,
                                                            int64_t rows, int64_t cols,
                                                            int64_t ld, float* __restrict__ partial) {
-  // 16-byte chunks per row; the host guarantees 16-byte aligned rows
   const int64_t elem = kBf16 ? 2 : 4;
-  const int64_t cpr = cols * elem / 16;
-  const int64_t total = rows * cpr;
-  const int64_t per = (total + gridDim.x - 1) / gridDim.x;
-  const int64_t beg = (int64_t)blockIdx.x * per;
-  const int64_t end = beg + per < total ? beg + per : total;
-  const char* base = (const char*)xv;
-  uint32_t m = 0;                        // max of |x| bit patterns (monotone for |x|)
-  int64_t i = beg + threadIdx.x;
-  if (i < end) {
-    int64_t r = i / cpr, c = i - r * cpr;
-    for (; i < end; i += blockDim.x) {
-      const u32x4 w = *(const u32x4*)(base + (r * ld * elem) + c * 16);
-      if (kBf16) {
+  const int64_t cpr = cols * elem / 16;             // 16-byte chunks per row (cols % 16 == 0)
+  uint32_t m = 0;
+  if (ld == cols) {
+    const u32x4* p = (const u32x4*)xv;
+    const int64_t n = rows * cpr;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += kAmaxUnroll * stride) {
+      u32x4 w[kAmaxUnroll];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t a = w[j] & 0x7FFF7FFFu;
-          m = max(m, max(a & 0xFFFFu, a >> 16));
-        }
-      } else {
+      for (int u = 0; u < kAmaxUnroll; ++u)
+        w[u] = i + u * stride < n ? p[i + u * stride] : u32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) m = max(m, w[j] & 0x7FFFFFFFu);
-      }
-      c += blockDim.x;
-      while (c >= cpr) { c -= cpr; ++r; }
+      for (int u = 0; u < kAmaxUnroll; ++u) m = fold_abs_bits(m, w[u], kBf16);
+    }
+  } else {
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+      const u32x4* p = (const u32x4*)((const char*)xv + r * ld * elem);
+      for (int64_t c = threadIdx.x; c < cpr; c += 256) m = fold_abs_bits(m, p[c], kBf16);
     }
   }
   float f = kBf16 ? __uint_as_float(m << 16) : __uint_as_float(m);
@@ -62,173 +81,214 @@ __global__ __launch_bounds__(256) void amax_partial_kernel(const void* __restric
 
 // ------------------------------------------------------------------ quantize pass
 
+// 8 values of a lane as fp32 from one 16-byte (bf16) or two 16-byte (fp32) loads.
+struct Raw8 {
+  u32x4 a, b;
+};
+
+// Unconditional loads (the caller clamps the offset into the tensor): keeping
+// them out of divergent branches lets the compiler wait for each one
+// separately instead of for all of them.
 template <bool kBf16>
-__device__ __forceinline__ void load_group(const void* xv, int64_t row_off, int64_t col0, int nblk,
-                                           float* v) {
+__device__ __forceinline__ Raw8 load8(const void* x, int64_t off) {
+  Raw8 r;
   if (kBf16) {
-    const uint16_t* p = (const uint16_t*)xv + row_off + col0;
+    r.a = *(const u32x4*)((const uint16_t*)x + off);
+    r.b = u32x4{0, 0, 0, 0};
+  } else {
+    r.a = *(const u32x4*)((const float*)x + off);
+    r.b = *(const u32x4*)((const float*)x + off + 4);
+  }
+  return r;
+}
+
+template <bool kBf16>
+__device__ __forceinline__ void unpack8(const Raw8& r, float* v) {
+  if (kBf16) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      if (b < nblk) {
-        const u32x4 w0 = *(const u32x4*)(p + 16 * b);
-        const u32x4 w1 = *(const u32x4*)(p + 16 * b + 8);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[16 * b + 2 * j] = bf16_lo(w0[j]);
-          v[16 * b + 2 * j + 1] = bf16_hi(w0[j]);
-          v[16 * b + 8 + 2 * j] = bf16_lo(w1[j]);
-          v[16 * b + 8 + 2 * j + 1] = bf16_hi(w1[j]);
-        }
-      }
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bf16_lo(r.a[j]);
+      v[2 * j + 1] = bf16_hi(r.a[j]);
     }
   } else {
-    const float* p = (const float*)xv + row_off + col0;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      if (b < nblk) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 w = *(const f32x4*)(p + 16 * b + 4 * q);
-          v[16 * b + 4 * q + 0] = w[0];
-          v[16 * b + 4 * q + 1] = w[1];
-          v[16 * b + 4 * q + 2] = w[2];
-          v[16 * b + 4 * q + 3] = w[3];
-        }
-      }
+    for (int j = 0; j < 4; ++j) {
+      v[j] = __uint_as_float(r.a[j]);
+      v[4 + j] = __uint_as_float(r.b[j]);
     }
   }
 }
 
-__device__ __forceinline__ float resolve_amax(const float* amax, const float* partial, int n) {
-  if (amax) return *amax;
+// Tensor amax from the amax pass's kAmaxPartials partials (the pass writes all
+// of them): every wave reads them with independent 16-byte loads, so no
+// workgroup barrier is needed.
+struct Partials {
+  f32x4 w[kAmaxPartials / 256];
+};
+
+__device__ __forceinline__ Partials load_partials(const float* partial) {
+  Partials r;
+  const f32x4* p = (const f32x4*)(partial + (kAmaxPartials / 64) * (threadIdx.x & 63));
+#pragma unroll
+  for (int u = 0; u < kAmaxPartials / 256; ++u) r.w[u] = p[u];
+  return r;
+}
+
+__device__ __forceinline__ float reduce_partials(const Partials& r) {
   float m = 0.0f;
-  for (int i = threadIdx.x & 63; i < n; i += 64) m = fmaxf(m, partial[i]);
+#pragma unroll
+  for (int u = 0; u < kAmaxPartials / 256; ++u)
+    m = fmaxf(m, fmaxf(fmaxf(r.w[u][0], r.w[u][1]), fmaxf(r.w[u][2], r.w[u][3])));
   return wave_max(m);
+}
+
+// rows == 0 or cols == 0: only s_g is published (1.0 unless amax says otherwise).
+__global__ __launch_bounds__(64) void publish_gscale_kernel(const float* __restrict__ amax,
+                                                            const float* __restrict__ partial,
+                                                            float* __restrict__ gscale) {
+  const float m = amax ? *amax : reduce_partials(load_partials(partial));
+  if (threadIdx.x == 0) *gscale = global_scale(m);
+}
+
+// The 8 row tasks of a lane.  kPre: s_g < 2^-100, x is scaled by 2^64 before
+// encoding (a tensor-uniform choice, so the two variants are separate code).
+template <bool kBf16, bool kTiled, bool kPre>
+__device__ __forceinline__ void quantize_tasks(const Raw8* raw, const TensorEnc& te, int64_t r0,
+                                               int64_t rows, bool cok, int j,
+                                               uint8_t* __restrict__ cp,
+                                               uint8_t* __restrict__ sp, int64_t c_step,
+                                               int64_t s_step) {
+#pragma unroll
+  for (int t = 0; t < kTasks; ++t) {
+    float v[8];
+    unpack8<kBf16>(raw[t], v);
+    float bm = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bm = fmaxf(bm, __builtin_fabsf(v[e]));
+    bm = pair_max(bm);
+    const uint32_t sb = block_scale_byte(bm, te);
+    const BlockEnc enc = make_block_enc(sb, te);
+    if (kPre) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= 0x1p64f;
+    }
+    const uint32_t cw = encode8(v, enc, te);
+    if (cok && r0 + 4 * t < rows) {
+      *(uint32_t*)(cp + t * c_step) = cw;
+      if ((j & 1) == 0) sp[t * s_step] = (uint8_t)sb;
+    }
+  }
 }
 
 template <bool kBf16, bool kTiled>
 __global__ __launch_bounds__(256) void quantize_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
-    const float* __restrict__ amax, const float* __restrict__ partial, int n_partial,
+    const float* __restrict__ amax, const float* __restrict__ partial,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gscale) {
-  const float s_g = global_scale(resolve_amax(amax, partial, n_partial));
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *gscale = s_g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t r = (int64_t)blockIdx.x * 64 + lane;
-  const int64_t g = (int64_t)blockIdx.y * 4 + wave;
-  const int64_t col0 = g * 64;
-  if (r >= rows || col0 >= cols) return;
-  const int64_t left = (cols - col0) / 16;
-  const int nblk = left >= 4 ? 4 : (int)left;
-  const double six_sg = 6.0 * (double)s_g;
+  const int j = lane & 15;
+  const int64_t c0 = (int64_t)blockIdx.y * kTile + 8 * j;
+  const int64_t r0 = (int64_t)blockIdx.x * kTile + 32 * wave + (lane >> 4);
+  const bool cok = c0 < cols;
 
-  float v[64];
-  load_group<kBf16>(x, r * ld, col0, nblk, v);
-  uint32_t cw[8];
-  uint32_t sw;
-  if (s_g < 0x1p-100f) quantize_group<true>(v, nblk, s_g, six_sg, cw, sw);
-  else quantize_group<false>(v, nblk, s_g, six_sg, cw, sw);
+  // partial maxima first: in-order completion then lets task 0 start as soon
+  // as its own load is in
+  Partials part;
+  if (!amax) part = load_partials(partial);
+  // rows >= 1 and cols >= 16 here; out-of-range lanes load a valid element and
+  // store nothing (both lanes of a block are in or out together)
+  const int64_t cl = cok ? c0 : cols - 8;
+  Raw8 raw[kTasks];
+#pragma unroll
+  for (int t = 0; t < kTasks; ++t) {
+    const int64_t r = r0 + 4 * t;
+    raw[t] = load8<kBf16>(x, (r < rows ? r : rows - 1) * ld + cl);
+  }
+  float s_g = global_scale(amax ? *amax : reduce_partials(part));
+  s_g = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_g)));   // uniform
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *gscale = s_g;
+  const TensorEnc te = make_tensor_enc(s_g);
 
-  uint8_t* cp = codes + r * (cols / 2) + g * 32;
-  if (nblk == 4) {
-    *(u32x4*)cp = u32x4{cw[0], cw[1], cw[2], cw[3]};
-    *(u32x4*)(cp + 16) = u32x4{cw[4], cw[5], cw[6], cw[7]};
-  } else {
-    for (int b = 0; b < nblk; ++b) *(u32x2*)(cp + 8 * b) = u32x2{cw[2 * b], cw[2 * b + 1]};
-  }
-  if (kTiled) {
-    const int64_t off = ((r >> 7) * (cols / 64) + g) * 512 + (r & 127) * 4;
-    *(uint32_t*)(scales + off) = sw;
-  } else {
-    uint8_t* sp = scales + r * (cols / 16) + g * 4;
-    if (nblk == 4 && (cols % 64) == 0) {
-      *(uint32_t*)sp = sw;
-    } else {
-      for (int b = 0; b < nblk; ++b) sp[b] = (uint8_t)(sw >> (8 * b));
-    }
-  }
+  // output addresses of task 0; task t is 4 t rows further down
+  const int64_t kb = c0 >> 4;                           // block index along the row
+  uint8_t* cp = codes + r0 * (cols / 2) + c0 / 2;
+  uint8_t* sp = scales + (kTiled ? ((r0 >> 7) * (cols / 64) + (kb >> 2)) * 512 +
+                                       (r0 & 127) * 4 + (kb & 3)
+                                 : r0 * (cols / 16) + kb);
+  const int64_t c_step = 4 * (cols / 2);
+  const int64_t s_step = kTiled ? 16 : 4 * (cols / 16);   // tiled: 128-row tiles hold all 8 tasks
+  if (te.pre != 1.0f)
+    quantize_tasks<kBf16, kTiled, true>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step);
+  else
+    quantize_tasks<kBf16, kTiled, false>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step);
 }
 
 // ------------------------------------------------------------------ dequantize
 
+// Same tiling as quantize: per lane and row, one dword of codes and one scale
+// byte in, 8 values out (16 or 32 bytes).
 template <bool kTiled, bool kOutBf16>
 __global__ __launch_bounds__(256) void dequantize_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ gscale, int64_t rows, int64_t cols, void* __restrict__ y,
     int64_t ld_y) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t r = (int64_t)blockIdx.x * 64 + lane;
-  const int64_t g = (int64_t)blockIdx.y * 4 + wave;
-  const int64_t col0 = g * 64;
-  if (r >= rows || col0 >= cols) return;
-  const int64_t left = (cols - col0) / 16;
-  const int nblk = left >= 4 ? 4 : (int)left;
-  const float s_g = *gscale;
+  const int j = lane & 15;
+  const int64_t c0 = (int64_t)blockIdx.y * kTile + 8 * j;
+  const int64_t r0 = (int64_t)blockIdx.x * kTile + 32 * wave + (lane >> 4);
+  if (c0 >= cols) return;
 
-  uint32_t sw;
-  if (kTiled) {
-    sw = *(const uint32_t*)(scales + ((r >> 7) * (cols / 64) + g) * 512 + (r & 127) * 4);
-  } else {
-    const uint8_t* sp = scales + r * (cols / 16) + g * 4;
-    if (nblk == 4 && (cols % 64) == 0) {
-      sw = *(const uint32_t*)sp;
-    } else {
-      sw = 0;
-      for (int b = 0; b < nblk; ++b) sw |= (uint32_t)sp[b] << (8 * b);
+  uint32_t cw[kTasks], sbyte[kTasks];
+#pragma unroll
+  for (int t = 0; t < kTasks; ++t) {
+    const int64_t r = r0 + 4 * t;
+    cw[t] = 0;
+    sbyte[t] = 0;
+    if (r < rows) {
+      cw[t] = *(const uint32_t*)(codes + r * (cols / 2) + c0 / 2);
+      const int64_t so = kTiled ? ((r >> 7) * (cols / 64) + (c0 >> 6)) * 512 + (r & 127) * 4 +
+                                      ((c0 >> 4) & 3)
+                                : r * (cols / 16) + (c0 >> 4);
+      sbyte[t] = scales[so];
     }
   }
-  const uint8_t* cp = codes + r * (cols / 2) + g * 32;
+  const float s_g = *gscale;
+  // bf16: RN32(q s_b s_g) can be a bf16 midpoint that RN_bf16 would then round
+  // the wrong way only for some s_g; decided once (uniform) for this s_g
+  const bool check = kOutBf16 && product_needs_check(s_g);
+
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    if (b < nblk) {
-      const u32x2 cw = *(const u32x2*)(cp + 8 * b);
-      const float s_b = e4m3_value((sw >> (8 * b)) & 0xFFu);
-      float out[16];
+  for (int t = 0; t < kTasks; ++t) {
+    const int64_t r = r0 + 4 * t;
+    if (r >= rows) continue;
+    const float s_b = e4m3_value(sbyte[t]);
+    float out[8];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int sel = 0; sel < 4; ++sel) {
-          const f32x2 q = e2m1_pair(cw[h], sel);
-          const float a0 = q[0] * s_b, a1 = q[1] * s_b;         // exact: <= 6 bits
-          if (kOutBf16) {
-            out[8 * h + 2 * sel] = mul_for_bf16(a0, s_g);
-            out[8 * h + 2 * sel + 1] = mul_for_bf16(a1, s_g);
-          } else {
-            out[8 * h + 2 * sel] = a0 * s_g;
-            out[8 * h + 2 * sel + 1] = a1 * s_g;
-          }
-        }
-      }
-      if (kOutBf16) {
-        uint16_t* yp = (uint16_t*)y + r * ld_y + col0 + 16 * b;
-        u32x4 p0, p1;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p0[j] = pack_bf16x2(out[2 * j], out[2 * j + 1]);
-          p1[j] = pack_bf16x2(out[8 + 2 * j], out[8 + 2 * j + 1]);
-        }
-        *(u32x4*)yp = p0;
-        *(u32x4*)(yp + 8) = p1;
+    for (int sel = 0; sel < 4; ++sel) {
+      const f32x2 q = e2m1_pair(cw[t], sel);
+      const float a0 = q[0] * s_b, a1 = q[1] * s_b;         // exact: <= 6 bits
+      if (check) {
+        out[2 * sel] = mul_for_bf16(a0, s_g);
+        out[2 * sel + 1] = mul_for_bf16(a1, s_g);
       } else {
-        float* yp = (float*)y + r * ld_y + col0 + 16 * b;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *(f32x4*)(yp + 4 * q4) =
-              f32x4{out[4 * q4], out[4 * q4 + 1], out[4 * q4 + 2], out[4 * q4 + 3]};
+        out[2 * sel] = a0 * s_g;
+        out[2 * sel + 1] = a1 * s_g;
       }
+    }
+    if (kOutBf16) {
+      u32x4 p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = pack_bf16x2(out[2 * e], out[2 * e + 1]);
+      *(u32x4*)((uint16_t*)y + r * ld_y + c0) = p;
+    } else {
+      float* yp = (float*)y + r * ld_y + c0;
+      *(f32x4*)yp = f32x4{out[0], out[1], out[2], out[3]};
+      *(f32x4*)(yp + 4) = f32x4{out[4], out[5], out[6], out[7]};
     }
   }
 }
 
 // ------------------------------------------------------------------ launchers
-
-static int amax_grid(int64_t rows, int64_t cols, bool bf16) {
-  const int64_t chunks = rows * cols * (bf16 ? 2 : 4) / 16;
-  int64_t g = (chunks + 255) / 256;
-  if (g > kAmaxPartials) g = kAmaxPartials;
-  if (g < 1) g = 1;
-  return (int)g;
-}
 
 size_t quantize_workspace_bytes(int64_t rows, int64_t cols, bool has_amax) {
   (void)rows;
@@ -240,31 +300,23 @@ void launch_quantize(const void* x, bool x_bf16, int64_t rows, int64_t cols, int
                      const float* amax, uint8_t* codes, uint8_t* scales, bool tiled,
                      float* gscale, void* workspace, hipStream_t stream) {
   float* partial = (float*)workspace;
-  int n_partial = 0;
   if (!amax) {
-    n_partial = amax_grid(rows, cols, x_bf16);
+    // always kAmaxPartials workgroups: every partial is written (idle ones write 0)
     if (x_bf16)
-      hipLaunchKernelGGL(amax_partial_kernel<true>, dim3(n_partial), dim3(256), 0, stream, x,
-                         rows, cols, ld, partial);
+      hipLaunchKernelGGL(amax_partial_kernel<true>, dim3(kAmaxPartials), dim3(256), 0, stream,
+                         x, rows, cols, ld, partial);
     else
-      hipLaunchKernelGGL(amax_partial_kernel<false>, dim3(n_partial), dim3(256), 0, stream, x,
-                         rows, cols, ld, partial);
+      hipLaunchKernelGGL(amax_partial_kernel<false>, dim3(kAmaxPartials), dim3(256), 0, stream,
+                         x, rows, cols, ld, partial);
   }
-  const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((cols / 16 + 15) / 16));
+  const dim3 grid((unsigned)((rows + kTile - 1) / kTile), (unsigned)((cols + kTile - 1) / kTile));
   if (rows == 0 || cols == 0) {
-    // still publish s_g (1.0 for an empty tensor) with a single idle lane group
-    const dim3 one(1, 1);
-    if (x_bf16)
-      hipLaunchKernelGGL((quantize_kernel<true, false>), one, dim3(256), 0, stream, x, rows,
-                         cols, ld, amax, partial, n_partial, codes, scales, gscale);
-    else
-      hipLaunchKernelGGL((quantize_kernel<false, false>), one, dim3(256), 0, stream, x, rows,
-                         cols, ld, amax, partial, n_partial, codes, scales, gscale);
+    hipLaunchKernelGGL(publish_gscale_kernel, dim3(1), dim3(64), 0, stream, amax, partial, gscale);
     return;
   }
 #define NVFP4_QLAUNCH(B, T)                                                                 \
   hipLaunchKernelGGL((quantize_kernel<B, T>), grid, dim3(256), 0, stream, x, rows, cols, ld, \
-                     amax, partial, n_partial, codes, scales, gscale)
+                     amax, partial, codes, scales, gscale)
   if (x_bf16) {
     if (tiled) NVFP4_QLAUNCH(true, true);
     else NVFP4_QLAUNCH(true, false);
@@ -279,7 +331,7 @@ void launch_dequantize(const uint8_t* codes, const uint8_t* scales, bool tiled,
                        const float* gscale, int64_t rows, int64_t cols, void* y, bool y_bf16,
                        int64_t ld_y, hipStream_t stream) {
   if (rows == 0 || cols == 0) return;
-  const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((cols / 16 + 15) / 16));
+  const dim3 grid((unsigned)((rows + kTile - 1) / kTile), (unsigned)((cols + kTile - 1) / kTile));
 #define NVFP4_DLAUNCH(T, B)                                                                  \
   hipLaunchKernelGGL((dequantize_kernel<T, B>), grid, dim3(256), 0, stream, codes, scales,   \
                      gscale, rows, cols, y, ld_y)
