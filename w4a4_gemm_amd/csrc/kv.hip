@@ -297,28 +297,177 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(
 //
 // A workgroup covers `tt` tokens of one listed page and all heads.  Thread
 // `pos` owns the unit position (head h, value group sub) of a token row and
-// walks the tile's tokens, so its K mean (both chunks a page can hold) stays
-// in registers and the loop carries no index arithmetic beyond strides.  The
-// output of a token is one contiguous run of H * D bf16 values, unit pos at
-// bytes [16 pos, 16 pos + 16): consecutive lanes store consecutive 16 bytes.
+// walks the tile's tokens, so its K mean stays in registers and the loop
+// carries no index arithmetic beyond strides.  The output of a token is one
+// contiguous run of H * D bf16 values, unit pos at bytes [16 pos, 16 pos + 16):
+// consecutive lanes store consecutive 16 bytes.
 //
 // Exact rounding at low cost: V^ = RN_bf16(a s_gV) needs the midpoint fix-up
 // only for the rare s_gV that product_needs_check() flags (decided once per
-// chunk); for K^ = RN_bf16(a s_gK + mu) the eight fp32 FMA results of a unit
-// are tested together and the exact slow path runs only when one of them is
-// a bf16 midpoint.
-template <int kTok>
+// tile, and the two cases are separate code); for K^ = RN_bf16(a s_gK + mu)
+// the eight fp32 FMA results of a unit are tested together and the exact slow
+// path runs only when one of them is a bf16 midpoint.
+
+struct UnitPtrs {
+  const uint8_t *kc, *ks, *vc, *vs;   // codes dword / scale byte of token 0 of the tile
+  int64_t c_stride, s_stride;          // bytes per token (row) in the codes / scale regions
+};
+
+// One token of one unit: 8 K and 8 V values.
+template <bool kVCheck>
+__device__ __forceinline__ void dequant_unit(uint32_t kcw, uint32_t ksb, uint32_t vcw,
+                                             uint32_t vsb, float sgk, float sgv, const float* mu,
+                                             uint16_t* ko_p, uint16_t* vo_p) {
+  const float sbk = e4m3_value(ksb), sbv = e4m3_value(vsb);
+  float ka[8], kf[8], vf[8];
+  uint32_t off = 0xFFFFFFFFu;
+#pragma unroll
+  for (int sel = 0; sel < 4; ++sel) {
+    const f32x2 qk = e2m1_pair(kcw, sel);
+    const f32x2 qv = e2m1_pair(vcw, sel);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int n = 2 * sel + e;
+      ka[n] = qk[e] * sbk;                                  // exact
+      kf[n] = __builtin_fmaf(ka[n], sgk, mu[n]);
+      off = min(off, off_midpoint(kf[n]));
+      vf[n] = kVCheck ? mul_for_bf16(qv[e] * sbv, sgv) : (qv[e] * sbv) * sgv;
+    }
+  }
+  if (__builtin_expect(off == 0u, 0)) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) kf[n] = fma_for_bf16(ka[n], sgk, mu[n]);
+  }
+  u32x4 ko, vo;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    ko[q] = pack_bf16x2(kf[2 * q], kf[2 * q + 1]);
+    vo[q] = pack_bf16x2(vf[2 * q], vf[2 * q + 1]);
+  }
+  *(u32x4*)ko_p = ko;
+  *(u32x4*)vo_p = vo;
+}
+
+// Fast path: all kTT tokens of the tile exist and belong to one chunk.
+template <int kTT, bool kVCheck>
+__device__ __forceinline__ void dequant_tile_uniform(const UnitPtrs& u, float sgk, float sgv,
+                                                     const float* mu, uint16_t* ko,
+                                                     uint16_t* vo, int64_t row_elems) {
+  uint32_t kcw[kTT], vcw[kTT], ksb[kTT], vsb[kTT];
+#pragma unroll
+  for (int j = 0; j < kTT; ++j) {
+    kcw[j] = *(const uint32_t*)(u.kc + j * u.c_stride);
+    vcw[j] = *(const uint32_t*)(u.vc + j * u.c_stride);
+    ksb[j] = u.ks[j * u.s_stride];
+    vsb[j] = u.vs[j * u.s_stride];
+  }
+#pragma unroll
+  for (int j = 0; j < kTT; ++j)
+    dequant_unit<kVCheck>(kcw[j], ksb[j], vcw[j], vsb[j], sgk, sgv, mu, ko + j * row_elems,
+                          vo + j * row_elems);
+}
+
+// ---- quad path (head_dim % 32 == 0): the four lanes of a quad own value groups
+// 4m..4m+3 of one head.  Lane k loads token k's 16 bytes of codes for those
+// four groups (one load instead of four), and a 4 x 4 dword transpose across
+// the quad (DPP lane swaps) gives each lane its own group for the 4 tokens.
+
+__device__ __forceinline__ uint32_t quad_swap1(uint32_t v) {      // value of lane ^ 1
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t quad_swap2(uint32_t v) {      // value of lane ^ 2
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+}
+template <int kLane>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {      // value of quad lane kLane
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kLane * 0x55, 0xF, 0xF, false);
+}
+
+// In: lane k (k = lane % 4) holds row k of a 4 x 4 matrix.  Out: column k.
+// Two butterfly stages; in stage b, element e is taken from lane k ^ 2^b
+// (its element e ^ 2^b) exactly when bit b of e and of k differ.
+__device__ __forceinline__ u32x4 quad_transpose(u32x4 a, int k) {
+  const bool o0 = k & 1, o1 = k & 2;
+  const uint32_t x0 = quad_swap1(a[1]), x1 = quad_swap1(a[0]);
+  const uint32_t x2 = quad_swap1(a[3]), x3 = quad_swap1(a[2]);
+  a = u32x4{o0 ? x0 : a[0], o0 ? a[1] : x1, o0 ? x2 : a[2], o0 ? a[3] : x3};
+  const uint32_t y0 = quad_swap2(a[2]), y1 = quad_swap2(a[3]);
+  const uint32_t y2 = quad_swap2(a[0]), y3 = quad_swap2(a[1]);
+  return u32x4{o1 ? y0 : a[0], o1 ? y1 : a[1], o1 ? a[2] : y2, o1 ? a[3] : y3};
+}
+
+// Scale byte of this lane's group for token j of the quad: lane j loaded the
+// two scale bytes (groups 4m..4m+3 span two blocks) of token j.
+template <int kJ>
+__device__ __forceinline__ uint32_t quad_scale(uint32_t two_bytes, int k) {
+  return (quad_bcast<kJ>(two_bytes) >> (8 * (k >> 1))) & 0xFFu;
+}
+
+// Fast path with the quad loads: kTT tokens (a multiple of 4), one chunk.
+// `u` points at this lane's own group of token 0; `q` at the quad's 16-byte
+// code block / 2-byte scale pair of token k (lane k of the quad).
+template <int kTT, bool kVCheck>
+__device__ __forceinline__ void dequant_tile_quad(const UnitPtrs& q, int k, float sgk, float sgv,
+                                                  const float* mu, uint16_t* ko, uint16_t* vo,
+                                                  int64_t row_elems) {
+  constexpr int kG = kTT / 4;
+  u32x4 kc[kG], vc[kG];
+  uint32_t ks[kG], vs[kG];
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    kc[g] = *(const u32x4*)(q.kc + 4 * g * q.c_stride);
+    vc[g] = *(const u32x4*)(q.vc + 4 * g * q.c_stride);
+    ks[g] = *(const uint16_t*)(q.ks + 4 * g * q.s_stride);
+    vs[g] = *(const uint16_t*)(q.vs + 4 * g * q.s_stride);
+  }
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    const u32x4 kt = quad_transpose(kc[g], k), vt = quad_transpose(vc[g], k);
+    uint16_t* kg = ko + 4 * g * row_elems;
+    uint16_t* vg = vo + 4 * g * row_elems;
+    dequant_unit<kVCheck>(kt[0], quad_scale<0>(ks[g], k), vt[0], quad_scale<0>(vs[g], k), sgk,
+                          sgv, mu, kg, vg);
+    dequant_unit<kVCheck>(kt[1], quad_scale<1>(ks[g], k), vt[1], quad_scale<1>(vs[g], k), sgk,
+                          sgv, mu, kg + row_elems, vg + row_elems);
+    dequant_unit<kVCheck>(kt[2], quad_scale<2>(ks[g], k), vt[2], quad_scale<2>(vs[g], k), sgk,
+                          sgv, mu, kg + 2 * row_elems, vg + 2 * row_elems);
+    dequant_unit<kVCheck>(kt[3], quad_scale<3>(ks[g], k), vt[3], quad_scale<3>(vs[g], k), sgk,
+                          sgv, mu, kg + 3 * row_elems, vg + 3 * row_elems);
+  }
+}
+
+__device__ __forceinline__ void load_mu8(const float* p, float* mu) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    mu[j] = a[j];
+    mu[4 + j] = b[j];
+  }
+}
+
+// Wave-uniform product_needs_check(g): lane l tests significand l % 16 and the
+// wave votes.  Every lane of the wave must be active.
+__device__ __forceinline__ bool needs_check_wave(float g) {
+  if (!(g >= 0x1p-116f)) return true;
+  const int i = threadIdx.x & 15;
+  const float a = ((i & 8) ? 1.5f : 1.0f) * (1.0f + (float)(i & 7) * 0.125f);
+  const float p = a * g;
+  const bool need = (__float_as_uint(p) & 0xFFFFu) == 0x8000u && __builtin_fmaf(a, g, -p) != 0.0f;
+  return __builtin_amdgcn_ballot_w64(need) != 0;
+}
+
+template <int kTT, bool kQuad>
 __global__ __launch_bounds__(512) void kv_dequant_kernel(KvGeom g, int64_t n_phys,
-                                                         const int32_t* __restrict__ pages, int tt,
+                                                         const int32_t* __restrict__ pages,
                                                          uint16_t* __restrict__ k_out,
                                                          uint16_t* __restrict__ v_out) {
   const int H = g.n_heads, D = g.head_dim, P = g.page_tokens;
   const int upr = D / 8;                                  // units per (token, head) row
   const int npos = H * upr;                               // units per token
-  const int tiles = (P + tt - 1) / tt;
+  const int tiles = (P + kTT - 1) / kTT;
   const int64_t i = blockIdx.x / tiles;
-  const int t0 = (blockIdx.x % tiles) * tt;
-  const int ntok = min(tt, P - t0);
+  const int t0 = (blockIdx.x % tiles) * kTT;
+  const int ntok = min(kTT, P - t0);
   const int32_t lp = pages[i];
   bool valid = lp >= 0 && lp < g.max_pages;
   const int64_t phys = valid ? (int64_t)g.page_table[lp] : -1;
@@ -337,9 +486,13 @@ __global__ __launch_bounds__(512) void kv_dequant_kernel(KvGeom g, int64_t n_phy
   const int split = g.page_chunk[2 * lp + 1];
   c0 = c0 < 0 ? 0 : (c0 >= g.max_chunks ? g.max_chunks - 1 : c0);
   const int c1 = c0 + 1 < g.max_chunks ? c0 + 1 : g.max_chunks - 1;
+  // tile entirely in one chunk (the common case) and complete
+  const bool uniform = ntok == kTT && (t0 + kTT <= split || t0 >= split);
+  const int cu = t0 >= split ? c1 : c0;
   const float sgk0 = g.k_gscale[c0], sgk1 = g.k_gscale[c1];
   const float sgv0 = g.v_gscale[c0], sgv1 = g.v_gscale[c1];
-  const bool vcheck = product_needs_check(sgv0) || product_needs_check(sgv1);
+  const bool vcheck = uniform ? needs_check_wave(cu == c0 ? sgv0 : sgv1)
+                              : needs_check_wave(sgv0) || needs_check_wave(sgv1);
 
   const uint8_t* page = g.pool + phys * g.page_bytes;
   const int64_t codes_region = (int64_t)H * P * (D / 2);
@@ -347,70 +500,58 @@ __global__ __launch_bounds__(512) void kv_dequant_kernel(KvGeom g, int64_t n_phy
 
   for (int pos = threadIdx.x; pos < npos; pos += blockDim.x) {
     const int h = pos / upr, sub = pos - (pos / upr) * upr;
-    float mu0[8], mu1[8];
-    {
-      const float* m0 = g.k_mean + ((int64_t)c0 * H + h) * D + 8 * sub;
-      const float* m1 = g.k_mean + ((int64_t)c1 * H + h) * D + 8 * sub;
-      const f32x4 a0 = *(const f32x4*)m0, a1 = *(const f32x4*)(m0 + 4);
-      const f32x4 b0 = *(const f32x4*)m1, b1 = *(const f32x4*)(m1 + 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        mu0[j] = a0[j]; mu0[4 + j] = a1[j];
-        mu1[j] = b0[j]; mu1[4 + j] = b1[j];
-      }
-    }
     const int64_t r0 = (int64_t)h * P + t0;                // (head, slot) row of token t0
-    const uint8_t* kc = page + r0 * (D / 2) + 4 * sub;
-    const uint8_t* ks = page + codes_region + r0 * (D / 16) + (sub >> 1);
-    const uint8_t* vc = page + codes_region + scales_region + r0 * (D / 2) + 4 * sub;
-    const uint8_t* vs = page + 2 * codes_region + scales_region + r0 * (D / 16) + (sub >> 1);
-    for (int t = 0; t < ntok; t += kTok) {
-      uint32_t kcw[kTok], vcw[kTok], ksb[kTok], vsb[kTok];
-#pragma unroll
-      for (int j = 0; j < kTok; ++j) {
-        if (t + j < ntok) {
-          kcw[j] = *(const uint32_t*)(kc + (int64_t)(t + j) * (D / 2));
-          vcw[j] = *(const uint32_t*)(vc + (int64_t)(t + j) * (D / 2));
-          ksb[j] = ks[(int64_t)(t + j) * (D / 16)];
-          vsb[j] = vs[(int64_t)(t + j) * (D / 16)];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kTok; ++j) {
-        if (t + j < ntok) {
-          const bool second = t0 + t + j >= split;
-          const float sgk = second ? sgk1 : sgk0, sgv = second ? sgv1 : sgv0;
-          const float sbk = e4m3_value(ksb[j]), sbv = e4m3_value(vsb[j]);
-          float ka[8], kf[8], vf[8];
-          uint32_t off = 0xFFFFFFFFu;
-#pragma unroll
-          for (int sel = 0; sel < 4; ++sel) {
-            const f32x2 qk = e2m1_pair(kcw[j], sel);
-            const f32x2 qv = e2m1_pair(vcw[j], sel);
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int n = 2 * sel + e;
-              ka[n] = qk[e] * sbk;                          // exact
-              kf[n] = __builtin_fmaf(ka[n], sgk, second ? mu1[n] : mu0[n]);
-              off = min(off, off_midpoint(kf[n]));
-              vf[n] = vcheck ? mul_for_bf16(qv[e] * sbv, sgv) : (qv[e] * sbv) * sgv;
-            }
-          }
-          if (__builtin_expect(off == 0u, 0)) {
-#pragma unroll
-            for (int n = 0; n < 8; ++n)
-              kf[n] = fma_for_bf16(ka[n], sgk, second ? mu1[n] : mu0[n]);
-          }
-          u32x4 ko, vo;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            ko[q] = pack_bf16x2(kf[2 * q], kf[2 * q + 1]);
-            vo[q] = pack_bf16x2(vf[2 * q], vf[2 * q + 1]);
-          }
-          const int64_t o = (int64_t)(t + j) * row_elems + 8 * pos;
-          *(u32x4*)(k_tile + o) = ko;
-          *(u32x4*)(v_tile + o) = vo;
-        }
+    UnitPtrs u;
+    u.kc = page + r0 * (D / 2) + 4 * sub;
+    u.ks = page + codes_region + r0 * (D / 16) + (sub >> 1);
+    u.vc = page + codes_region + scales_region + r0 * (D / 2) + 4 * sub;
+    u.vs = page + 2 * codes_region + scales_region + r0 * (D / 16) + (sub >> 1);
+    u.c_stride = D / 2;
+    u.s_stride = D / 16;
+    const int64_t mu_off = (int64_t)h * D + 8 * sub;
+    if (kQuad && uniform) {
+      // head_dim % 32 == 0 and the block size a multiple of 64: quads are whole
+      const int k = pos & 3;
+      const int64_t rq = r0 + k;                            // token k of the quad
+      UnitPtrs q;
+      q.kc = page + rq * (D / 2) + 16 * (sub >> 2);
+      q.ks = page + codes_region + rq * (D / 16) + 2 * (sub >> 2);
+      q.vc = page + codes_region + scales_region + rq * (D / 2) + 16 * (sub >> 2);
+      q.vs = page + 2 * codes_region + scales_region + rq * (D / 16) + 2 * (sub >> 2);
+      q.c_stride = D / 2;
+      q.s_stride = D / 16;
+      float mu[8];
+      load_mu8(g.k_mean + (int64_t)cu * H * D + mu_off, mu);
+      const float sgk = cu == c0 ? sgk0 : sgk1, sgv = cu == c0 ? sgv0 : sgv1;
+      if (vcheck)
+        dequant_tile_quad<kTT, true>(q, k, sgk, sgv, mu, k_tile + 8 * pos, v_tile + 8 * pos,
+                                     row_elems);
+      else
+        dequant_tile_quad<kTT, false>(q, k, sgk, sgv, mu, k_tile + 8 * pos, v_tile + 8 * pos,
+                                      row_elems);
+    } else if (uniform) {
+      float mu[8];
+      load_mu8(g.k_mean + (int64_t)cu * H * D + mu_off, mu);
+      const float sgk = cu == c0 ? sgk0 : sgk1, sgv = cu == c0 ? sgv0 : sgv1;
+      if (vcheck)
+        dequant_tile_uniform<kTT, true>(u, sgk, sgv, mu, k_tile + 8 * pos, v_tile + 8 * pos,
+                                        row_elems);
+      else
+        dequant_tile_uniform<kTT, false>(u, sgk, sgv, mu, k_tile + 8 * pos, v_tile + 8 * pos,
+                                         row_elems);
+    } else {
+      // ragged tile or a tile across the chunk boundary: token by token
+      float mu0[8], mu1[8];
+      load_mu8(g.k_mean + (int64_t)c0 * H * D + mu_off, mu0);
+      load_mu8(g.k_mean + (int64_t)c1 * H * D + mu_off, mu1);
+      for (int t = 0; t < ntok; ++t) {
+        const bool second = t0 + t >= split;
+        const uint32_t kcw = *(const uint32_t*)(u.kc + t * u.c_stride);
+        const uint32_t vcw = *(const uint32_t*)(u.vc + t * u.c_stride);
+        const uint32_t ksb = u.ks[t * u.s_stride], vsb = u.vs[t * u.s_stride];
+        dequant_unit<true>(kcw, ksb, vcw, vsb, second ? sgk1 : sgk0, second ? sgv1 : sgv0,
+                           second ? mu1 : mu0, k_tile + t * row_elems + 8 * pos,
+                           v_tile + t * row_elems + 8 * pos);
       }
     }
   }
@@ -434,16 +575,30 @@ void launch_kv_quantize(const KvGeom& g, int32_t chunk_id, const uint16_t* k, co
                      chunk_id, ws, nsw, nfw, g, g.n_phys_pages, (const float*)mu);
 }
 
+#ifndef NVFP4_KV_READ_TOKENS
+#define NVFP4_KV_READ_TOKENS 8
+#endif
+
 void launch_kv_dequant(const KvGeom& g, const int32_t* logical_pages, int32_t n_pages,
                        uint16_t* k_out, uint16_t* v_out, hipStream_t stream) {
-  // one thread per unit position of a token row (up to 512), 16 tokens per workgroup
+  // One thread per unit position of a token row (up to 512) and a few tokens
+  // per workgroup: each workgroup then writes short contiguous runs (H * D * 2
+  // bytes per token for K and for V), and the chip's concurrent writes stay
+  // close together, which sustains a higher HBM write rate than long
+  // per-workgroup runs.
+  constexpr int kTT = NVFP4_KV_READ_TOKENS;
   const int npos = g.n_heads * (g.head_dim / 8);
   int threads = ((npos + 63) / 64) * 64;
   threads = threads > 512 ? 512 : threads;
-  const int tt = g.page_tokens < 16 ? g.page_tokens : 16;
-  const int64_t tiles = (g.page_tokens + tt - 1) / tt;
-  hipLaunchKernelGGL(kv_dequant_kernel<4>, dim3((unsigned)(tiles * n_pages)), dim3(threads), 0,
-                     stream, g, g.n_phys_pages, logical_pages, tt, k_out, v_out);
+  const int64_t tiles = (g.page_tokens + kTT - 1) / kTT;
+  // quad loads need whole quads of value groups per head (head_dim % 32) and
+  // lanes that line up with them (block size a multiple of 4, which 64 is)
+  if (g.head_dim % 32 == 0 && kTT % 4 == 0)
+    hipLaunchKernelGGL((kv_dequant_kernel<kTT, true>), dim3((unsigned)(tiles * n_pages)),
+                       dim3(threads), 0, stream, g, g.n_phys_pages, logical_pages, k_out, v_out);
+  else
+    hipLaunchKernelGGL((kv_dequant_kernel<kTT, false>), dim3((unsigned)(tiles * n_pages)),
+                       dim3(threads), 0, stream, g, g.n_phys_pages, logical_pages, k_out, v_out);
 }
 
 }  // namespace nvfp4
