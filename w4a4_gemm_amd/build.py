@@ -35,6 +35,8 @@ COMMON = [
     "-fPIC",
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # NewGVN: the classic GVN pass takes minutes on the unrolled GEMM main loop
+    "-mllvm", "-enable-newgvn=true",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]

@@ -4,17 +4,21 @@
 // report summary, section 四, first key).  gfx950's scaled FP4 MFMA takes
 // power-of-two (E8M0) scales per 32 values, which cannot carry NVFP4's E4M3
 // scale per 16 values exactly.  Instead every product q s_b is formed exactly
-// in bf16 (q has <= 2 significant bits, s_b <= 4, so q s_b fits bf16's 8) and
-// fed to the bf16 MFMA, whose products are exact in fp32; only the fp32
-// accumulation and the final multiply by s_gx s_gw round.
+// in fp16 and fed to the fp16 MFMA: q has <= 2 significant bits and s_b <= 4,
+// so q s_b has <= 6 (fp16 keeps 11), and |q s_b| lies in [2^-10, 2688], inside
+// fp16's normal range.  The MFMA products are exact in fp32; only the fp32
+// accumulation and the final multiply by s_gx s_gw round.  Decoding is two
+// instructions per two values: gfx950's fp4 -> fp16 pair conversion and one
+// packed fp16 multiply by s_b (both exact, as above, and checked on the device
+// over every code and scale byte).
 //
 // Work decomposition
 //   * workgroup tile 256 x BN (BN = 256 or 192), K step 64; four waves in a
 //     2 x 2 grid, each owning a 128 x BN/2 block of 32 x 32 accumulators
-//     (v_mfma_f32_32x32x16_bf16).
+//     (v_mfma_f32_32x32x16_f16).
 //   * Each K step a thread fetches one 64-value slice of one X row and one W
 //     row (32 bytes of codes + one scale dword, read straight from either
-//     scale layout), decodes it in registers to 64 bf16 and writes it to LDS.
+//     scale layout), decodes it in registers to 64 fp16 and writes it to LDS.
 //     Decoding happens once per workgroup per element; the MFMA operands are
 //     then read from LDS with 16-byte loads.  Rows are padded to 144 bytes so
 //     that both the stores and the fragment loads are free of bank conflicts.
@@ -32,12 +36,13 @@ namespace nvfp4 {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 256;
 constexpr int kBK = 64;
-constexpr int kLdsRow = kBK + 8;          // bf16 per padded LDS row (144 bytes)
+constexpr int kLdsRow = kBK + 8;          // fp16 per padded LDS row (144 bytes)
 constexpr int kThreads = 256;
 
 struct Operand {
@@ -79,32 +84,41 @@ __device__ __forceinline__ Slice fetch(const RowSrc& rs, int ks) {
   return sl;
 }
 
-// 8 codes (one dword) times s_b -> 4 dwords of bf16 pairs.  The products are
-// exact fp32 numbers with <= 6 significant bits, so their top halves are the
-// exact bf16 values.
-__device__ __forceinline__ void decode8(uint32_t w, float s_b, uint32_t* out) {
-#define NVFP4_DEC(SEL)                                                                 \
-  {                                                                                    \
-    const f32x2 q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);            \
-    const uint32_t lo = __float_as_uint(q[0] * s_b), hi = __float_as_uint(q[1] * s_b); \
-    out[SEL] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);                             \
-  }
-  NVFP4_DEC(0)
-  NVFP4_DEC(1)
-  NVFP4_DEC(2)
-  NVFP4_DEC(3)
-#undef NVFP4_DEC
+// Codes byte SEL of w (two values) times s_b (half HI of the fp16 pair sp):
+// one fp4 -> fp16 pair conversion and one packed multiply, both exact
+// (products of <= 6 significant bits).
+template <int SEL>
+__device__ __forceinline__ uint32_t dec2(uint32_t w, uint32_t sp, int hi) {
+  const _Float16 s_b = __builtin_bit_cast(f16x2, sp)[hi];
+  const f16x2 q = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+  return __builtin_bit_cast(uint32_t, q * (f16x2){s_b, s_b});
+}
+
+// 8 codes (one dword) times s_b -> 4 dwords of fp16 pairs.
+__device__ __forceinline__ void decode8(uint32_t w, uint32_t sp, int hi, uint32_t* out) {
+  out[0] = dec2<0>(w, sp, hi);
+  out[1] = dec2<1>(w, sp, hi);
+  out[2] = dec2<2>(w, sp, hi);
+  out[3] = dec2<3>(w, sp, hi);
+}
+
+// The four E4M3 scale bytes of a dword as two fp16 pairs (exact: E4M3 fits
+// fp16): p[0] = blocks 0, 1; p[1] = blocks 2, 3.
+__device__ __forceinline__ void scales4(uint32_t s, uint32_t* p) {
+  p[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, false));
+  p[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, true));
 }
 
 __device__ __forceinline__ void decode_to_lds(const Slice& sl, uint16_t* row) {
   const uint32_t cw[8] = {sl.c0[0], sl.c0[1], sl.c0[2], sl.c0[3],
                           sl.c1[0], sl.c1[1], sl.c1[2], sl.c1[3]};
+  uint32_t sp[2];
+  scales4(sl.s, sp);
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const float s_b = e4m3_value((sl.s >> (8 * b)) & 0xFFu);
     uint32_t o[8];
-    decode8(cw[2 * b], s_b, o);
-    decode8(cw[2 * b + 1], s_b, o + 4);
+    decode8(cw[2 * b], sp[b >> 1], b & 1, o);
+    decode8(cw[2 * b + 1], sp[b >> 1], b & 1, o + 4);
     *(u32x4*)(row + 16 * b) = u32x4{o[0], o[1], o[2], o[3]};
     *(u32x4*)(row + 16 * b + 8) = u32x4{o[4], o[5], o[6], o[7]};
   }
@@ -129,13 +143,14 @@ __device__ __forceinline__ void tile_of(int bid, int nbm, int nbn, int& tm, int&
 __device__ __forceinline__ void decode_half(const Slice& sl, int half, uint16_t* __restrict__ row) {
   const uint32_t cw[8] = {sl.c0[0], sl.c0[1], sl.c0[2], sl.c0[3],
                           sl.c1[0], sl.c1[1], sl.c1[2], sl.c1[3]};
+  uint32_t sp[2];
+  scales4(sl.s, sp);
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
     const int b = 2 * half + bb;
-    const float s_b = e4m3_value((sl.s >> (8 * b)) & 0xFFu);
     uint32_t o[8];
-    decode8(cw[2 * b], s_b, o);
-    decode8(cw[2 * b + 1], s_b, o + 4);
+    decode8(cw[2 * b], sp[b >> 1], b & 1, o);
+    decode8(cw[2 * b + 1], sp[b >> 1], b & 1, o + 4);
     *(u32x4*)(row + 16 * b) = u32x4{o[0], o[1], o[2], o[3]};
     *(u32x4*)(row + 16 * b + 8) = u32x4{o[4], o[5], o[6], o[7]};
   }
@@ -143,7 +158,7 @@ __device__ __forceinline__ void decode_half(const Slice& sl, int half, uint16_t*
 
 template <int TM, int TN, int WN>
 struct Frags {
-  bf16x8 a[TM], b[TN];
+  f16x8 a[TM], b[TN];
 };
 
 template <int TM, int TN, int WN>
@@ -153,10 +168,10 @@ __device__ __forceinline__ void load_frags(Frags<TM, TN, WN>& f, const uint16_t*
   const int kc = kk * 16 + (lane >> 5) * 8;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
-    f.a[i] = *(const bf16x8*)(As + (wm * 128 + i * 32 + (lane & 31)) * kLdsRow + kc);
+    f.a[i] = *(const f16x8*)(As + (wm * 128 + i * 32 + (lane & 31)) * kLdsRow + kc);
 #pragma unroll
   for (int j = 0; j < TN; ++j)
-    f.b[j] = *(const bf16x8*)(Bs + (wn * WN + j * 32 + (lane & 31)) * kLdsRow + kc);
+    f.b[j] = *(const f16x8*)(Bs + (wn * WN + j * 32 + (lane & 31)) * kLdsRow + kc);
 }
 
 // One K step, software-pipelined, with an explicit instruction order.
@@ -164,8 +179,8 @@ __device__ __forceinline__ void load_frags(Frags<TM, TN, WN>& f, const uint16_t*
 // On entry `f0` holds the fragments of k16 sub-step 0 of stage As/Bs.  The
 // step issues TM*TN*4 MFMAs.  Between consecutive MFMAs it places a slice of
 // the decode of the next step (16 units: the 8 code dwords of the X slice and
-// the 8 of the W slice, each 4 x {fp4->fp32 pair, 2 exact multiplies, bf16
-// pack} plus one 16-byte LDS store into stage An), and during the first MFMAs
+// the 8 of the W slice, each 4 x {fp4->fp16 pair, one packed multiply} plus
+// one 16-byte LDS store into stage An), and during the first MFMAs
 // of sub-step kk the fragment loads of kk+1.  Scheduling fences keep that
 // order: an MFMA occupies the matrix pipe for 32 cycles, and the VALU work that
 // follows it in program order issues underneath instead of queueing behind the
@@ -188,12 +203,9 @@ __device__ __forceinline__ void gemm_step(f32x16 (&acc)[TM][TN], Frags<TM, TN, W
   const uint32_t cw[16] = {ca.c0[0], ca.c0[1], ca.c0[2], ca.c0[3], ca.c1[0], ca.c1[1],
                            ca.c1[2], ca.c1[3], cb.c0[0], cb.c0[1], cb.c0[2], cb.c0[3],
                            cb.c1[0], cb.c1[1], cb.c1[2], cb.c1[3]};
-  float sc[8];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    sc[b] = e4m3_value((ca.s >> (8 * b)) & 0xFFu);
-    sc[4 + b] = e4m3_value((cb.s >> (8 * b)) & 0xFFu);
-  }
+  uint32_t sc[4];                                  // fp16 scale pairs: X blocks 0-1, 2-3, W 0-1, 2-3
+  scales4(ca.s, sc);
+  scales4(cb.s, sc + 2);
   uint16_t* rowA = An + tid * kLdsRow;
   uint16_t* rowB = An + (kBM + tid) * kLdsRow;
   uint32_t out[4];
@@ -210,12 +222,12 @@ __device__ __forceinline__ void gemm_step(f32x16 (&acc)[TM][TN], Frags<TM, TN, W
       // fragment load for sub-step kk+1 (one per MFMA until all are issued)
       if (kk + 1 < kSub && m < TM + TN) {
         if (m < TM)
-          nxt.a[m] = *(const bf16x8*)(As + (wm * 128 + m * 32 + (lane & 31)) * kLdsRow + kc);
+          nxt.a[m] = *(const f16x8*)(As + (wm * 128 + m * 32 + (lane & 31)) * kLdsRow + kc);
         else
           nxt.b[m - TM] =
-              *(const bf16x8*)(Bs + (wn * WN + (m - TM) * 32 + (lane & 31)) * kLdsRow + kc);
+              *(const f16x8*)(Bs + (wn * WN + (m - TM) * 32 + (lane & 31)) * kLdsRow + kc);
       }
-      acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+      acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
           cur.a[m / TN], cur.b[m % TN], acc[m / TN][m % TN], 0, 0, 0);
       // decode slice: unit u, part p of kMpu; the 4 selectors of the unit's code
       // dword are split over the parts
@@ -224,13 +236,12 @@ __device__ __forceinline__ void gemm_step(f32x16 (&acc)[TM][TN], Frags<TM, TN, W
 #pragma unroll
       for (int sel = 0; sel < 4; ++sel) {
         if (sel >= sel0 && sel < sel1) {
-          const float s_b = sc[(u >> 3) * 4 + ((u & 7) >> 1)];
-          const f32x2 q = sel == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u], 1.0f, 0)
-                        : sel == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u], 1.0f, 1)
-                        : sel == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u], 1.0f, 2)
-                                   : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u], 1.0f, 3);
-          const uint32_t lo = __float_as_uint(q[0] * s_b), hi = __float_as_uint(q[1] * s_b);
-          out[sel] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+          const int blk = (u & 7) >> 1;            // block of code dword u within its slice
+          const uint32_t sp = sc[(u >> 3) * 2 + (blk >> 1)];
+          out[sel] = sel == 0 ? dec2<0>(cw[u], sp, blk & 1)
+                   : sel == 1 ? dec2<1>(cw[u], sp, blk & 1)
+                   : sel == 2 ? dec2<2>(cw[u], sp, blk & 1)
+                              : dec2<3>(cw[u], sp, blk & 1);
         }
       }
       if (p == kMpu - 1) {
@@ -238,6 +249,33 @@ __device__ __forceinline__ void gemm_step(f32x16 (&acc)[TM][TN], Frags<TM, TN, W
         *(u32x4*)(row + 8 * (u & 7)) = u32x4{out[0], out[1], out[2], out[3]};
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// One 32 x 32 accumulator tile to Y (lane: column lane % 32; register r:
+// row (r / 4) * 8 + (lane / 32) * 4 + r % 4), also folding max |Y| as stored.
+// Every element is bounds-checked (measured faster here than a separate
+// unchecked path for whole tiles).
+template <bool kOutBf16>
+__device__ __forceinline__ void store_tile(const f32x16& a, float scale, void* y, int64_t ld_y,
+                                           int row0, int col0, int M, int N, int lane,
+                                           float& amax) {
+  const int col = col0 + (lane & 31);
+  const int rbase = row0 + (lane >> 5) * 4;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = rbase + (r >> 2) * 8 + (r & 3);
+    const float v = a[r] * scale;
+    if (row < M && col < N) {
+      if (kOutBf16) {
+        const uint32_t b = f32_to_bf16_bits(v);
+        ((uint16_t*)y)[(int64_t)row * ld_y + col] = (uint16_t)b;
+        amax = fmaxf(amax, __builtin_fabsf(__uint_as_float(b << 16)));
+      } else {
+        ((float*)y)[(int64_t)row * ld_y + col] = v;
+        amax = fmaxf(amax, __builtin_fabsf(v));
+      }
     }
   }
 }
@@ -251,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_kernel(
     int nbn) {
   constexpr int WN = BN / 2;                // wave tile 128 x WN
   constexpr int TM = 4, TN = WN / 32;
-  constexpr int kStage = 2 * kBM * kLdsRow;  // bf16 per LDS stage: 256 A rows + 256 B rows
+  constexpr int kStage = 2 * kBM * kLdsRow;  // fp16 per LDS stage: 256 A rows + 256 B rows
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
   int tm, tn;
@@ -309,22 +347,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_kernel(
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int col = tn * BN + wn * WN + j * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = tm * kBM + wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const float v = acc[i][j][r] * scale;
-        if (row < M && col < N) {
-          if (kOutBf16) {
-            const uint32_t b = f32_to_bf16_bits(v);
-            ((uint16_t*)y)[(int64_t)row * ld_y + col] = (uint16_t)b;
-            amax = fmaxf(amax, __builtin_fabsf(__uint_as_float(b << 16)));
-          } else {
-            ((float*)y)[(int64_t)row * ld_y + col] = v;
-            amax = fmaxf(amax, __builtin_fabsf(v));
-          }
-        }
-      }
+      const int row0 = tm * kBM + wm * 128 + i * 32, col0 = tn * BN + wn * WN + j * 32;
+      store_tile<kOutBf16>(acc[i][j], scale, y, ld_y, row0, col0, M, N, lane, amax);
     }
   }
   if (y_amax) {
