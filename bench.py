@@ -17,15 +17,24 @@ One step is one pass of the whole hot path over resident synthetic inputs:
 The metric is the whole step as a percentage of the MI355X roofline: the time
 the step's algorithmic work takes at the roofline (HBM 8 TB/s for the
 bandwidth kernels -- one read of every input and one write of every output --
-and the 2.5 PFLOP/s dense bf16 MFMA peak for the GEMMs) divided by the
+and the 2.5 PFLOP/s dense fp16 MFMA peak for the GEMMs, which run on the
+fp16 MFMA) divided by the
 measured step time.  Per-op rates (GB/s, TFLOP/s) and fractions are reported
 alongside, plus the roofline of the dominant kernel (the FFN GEMM1 launch)
 and the CPU oracle's rate on a bounded sample of the same work.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --only OP [--reps N]     one op of the step, N times (profiling)
+       python bench.py --copy-bytes B [--reps N] a plain device copy of B bytes, N times
+                                                 (calibrates the HBM byte counters)
+
+roofline.traffic is the HBM traffic of one FFN GEMM1 launch as measured by
+rocprofv3 counters (profiles/ffn_gemm1_hbm_traffic.md); it is reported only
+while the GEMM source is the one those counters were taken with, else null.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -38,7 +47,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_BPS = 8.0e12               # MI355X HBM3E peak, bytes/s
-MFMA_BF16_FLOPS = 2.5e15       # MI355X dense bf16 MFMA peak, FLOP/s
+MFMA_F16_FLOPS = 2.5e15        # MI355X dense fp16 (and bf16) MFMA peak, FLOP/s
+GEMM_SOURCE = os.path.join(ROOT, "w4a4_gemm_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_gemm1_hbm_traffic.md")
 METRIC = "W4A4 GEMM TFLOPS + quant/dequant/KV GB/s, as % of MI355X roofline"
 
 NV_ELEM = 0.5625               # NVFP4 bytes per element (4-bit code + E4M3 per 16)
@@ -71,7 +82,7 @@ def op_table():
 
 def roofline_seconds(op):
     if "flops" in op:
-        return op["flops"] / MFMA_BF16_FLOPS
+        return op["flops"] / MFMA_F16_FLOPS
     return op["bytes"] / HBM_BPS
 
 
@@ -129,32 +140,43 @@ class Workload:
         n = self.window.numel() * r.P
         self.kh = torch.empty((n, r.H, r.D), dtype=torch.bfloat16, device=dev)
         self.vh = torch.empty((n, r.H, r.D), dtype=torch.bfloat16, device=dev)
+        self._ops = self.ops()
         torch.cuda.synchronize()
+
+    def ops(self):
+        """The step's ops in order, as (name, callable) pairs."""
+        nv = self.nv
+
+        def ffn_gemm1():
+            nv.nvfp4_gemm_w4a4(self.fxq, self.fw1, out=self.fy1, y_amax=self.famax)
+
+        def ffn_quantize():
+            nv.nvfp4_quantize(self.fx, out=self.fxq, workspace=self.fws)
+            self.famax.zero_()             # GEMM1 folds max|Y1| into a zeroed float
+
+        def kv_read():
+            for layer in range(self.lc_layers):
+                nv.nvfp4_kv_dequant_blocks(self.lc, layer, self.window, self.kh, self.vh)
+
+        return [
+            ("attn_quantize", lambda: nv.nvfp4_quantize(self.ax, out=self.axq, workspace=self.aws)),
+            ("attn_gemm", lambda: nv.nvfp4_gemm_w4a4(self.axq, self.aw, out=self.ay)),
+            ("attn_dequantize", lambda: nv.nvfp4_dequantize(self.axq, out=self.adq)),
+            ("ffn_quantize", ffn_quantize),
+            ("ffn_gemm1", ffn_gemm1),
+            ("ffn_requantize", lambda: nv.nvfp4_quantize(self.fy1, out=self.fy1q, amax=self.famax)),
+            ("ffn_gemm2", lambda: nv.nvfp4_gemm_w4a4(self.fy1q, self.fw2, out=self.fy2)),
+            ("kv_write", lambda: nv.nvfp4_kv_quantize(self.kv_w, 0, 0, self.kv_k, self.kv_v, 0,
+                                                      workspace=self.kv_ws)),
+            ("kv_read", kv_read),
+        ]
 
     def step(self, ev=None):
         """One pass of the hot path.  ``ev(name)`` records a timing event boundary."""
-        nv, torch = self.nv, self.torch
         mark = ev or (lambda name: None)
-        mark("attn_quantize")
-        nv.nvfp4_quantize(self.ax, out=self.axq, workspace=self.aws)
-        mark("attn_gemm")
-        nv.nvfp4_gemm_w4a4(self.axq, self.aw, out=self.ay)
-        mark("attn_dequantize")
-        nv.nvfp4_dequantize(self.axq, out=self.adq)
-        mark("ffn_quantize")
-        nv.nvfp4_quantize(self.fx, out=self.fxq, workspace=self.fws)
-        mark("ffn_gemm1")
-        self.famax.zero_()
-        nv.nvfp4_gemm_w4a4(self.fxq, self.fw1, out=self.fy1, y_amax=self.famax)
-        mark("ffn_requantize")
-        nv.nvfp4_quantize(self.fy1, out=self.fy1q, amax=self.famax)
-        mark("ffn_gemm2")
-        nv.nvfp4_gemm_w4a4(self.fy1q, self.fw2, out=self.fy2)
-        mark("kv_write")
-        nv.nvfp4_kv_quantize(self.kv_w, 0, 0, self.kv_k, self.kv_v, 0, workspace=self.kv_ws)
-        mark("kv_read")
-        for layer in range(self.lc_layers):
-            nv.nvfp4_kv_dequant_blocks(self.lc, layer, self.window, self.kh, self.vh)
+        for name, fn in self._ops:
+            mark(name)
+            fn()
         mark(None)
 
 
@@ -253,6 +275,55 @@ def cpu_baseline(ops):
     }
 
 
+# ------------------------------------------------------------------ measured traffic
+
+def source_sha256(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes of one FFN GEMM1 launch from the committed counter summary, or
+    None when it is missing or was taken with a different GEMM source."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if line.startswith("- ") and ":" in line:
+                    k, v = line[2:].split(":", 1)
+                    fields[k.strip()] = v.strip().strip("`")
+        if fields.get("gemm.hip sha256") != source_sha256(GEMM_SOURCE):
+            return None
+        return int(fields["HBM bytes per launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def run_only(name, reps, warmup):
+    import torch
+    wl = Workload(torch.device("cuda", 0))
+    fn = dict(wl.ops())[name]
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    print(json.dumps({"op": name, "reps": reps,
+                      "ms_per_rep": round((time.perf_counter() - t0) / reps * 1e3, 4)}), flush=True)
+
+
+def run_copy(nbytes, reps):
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
 # ------------------------------------------------------------------ main
 
 def main():
@@ -261,11 +332,20 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None, help="run one op of the step (profiling)")
+    ap.add_argument("--copy-bytes", type=int, default=0, help="plain copy (counter calibration)")
+    ap.add_argument("--reps", type=int, default=5)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the hot path runs on one MI355X; see the sharding notes).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_bytes:
+        run_copy(args.copy_bytes, args.reps)
+        return
+    if args.only:
+        run_only(args.only, args.reps, args.warmup)
+        return
 
     ops = op_table()
     wall, per_op = run_gpu(args.steps, args.warmup)
@@ -295,7 +375,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {
             "workload": ("DiT block hot path: attn proj quantize+GEMM 4096x3072x3072, dequantize, "
@@ -304,13 +384,13 @@ def main():
             "roofline_seconds_per_step": roof,
         },
         "roofline": {
-            "kernel": "gemm_w4a4_kernel (FFN GEMM1 launch, M8192 N14336 K3072, bf16 out)",
+            "kernel": "gemm_w4a4_kernel (FFN GEMM1 launch, M8192 N14336 K3072, fp16 MFMA, bf16 out)",
             "bound": "mfma",
             "achieved": round(ops["ffn_gemm1"]["flops"] / g1 / 1e12, 2),
-            "peak": MFMA_BF16_FLOPS / 1e12,
+            "peak": MFMA_F16_FLOPS / 1e12,
             "unit": "TFLOP/s",
-            "frac": round(ops["ffn_gemm1"]["flops"] / g1 / MFMA_BF16_FLOPS, 4),
-            "traffic": None,
+            "frac": round(ops["ffn_gemm1"]["flops"] / g1 / MFMA_F16_FLOPS, 4),
+            "traffic": measured_traffic(),
         },
         "per_op": per,
     }
