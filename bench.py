@@ -227,8 +227,10 @@ def cpu_baseline(ops):
     except Exception:
         blas_threads = 1
 
+    # sample sizes chosen for roughly 10-30 s of oracle work on the host
+    q_rows, g_rows, kv_tok, kv_pages = 2048, 512, 7040, 28
     a = synth.attn_proj()
-    x = F.bf16_bits_to_f64(a["x"][:256])                  # 256 x 3072 activation rows
+    x = F.bf16_bits_to_f64(a["x"][:q_rows])               # activation rows
     t = time.perf_counter()
     xq = Q.quantize(x)
     t_q = (time.perf_counter() - t) / x.size              # s per element
@@ -236,18 +238,18 @@ def cpu_baseline(ops):
     Q.dequantize(xq, "bf16")
     t_dq = (time.perf_counter() - t) / x.size
     wq = Q.quantize(F.bf16_bits_to_f64(a["w"]))
-    xg = Q.NVFP4(xq.packed[:64], xq.scales[:64], xq.s_g)  # 64 x 3072 x 3072 product
+    xg = Q.NVFP4(xq.packed[:g_rows], xq.scales[:g_rows], xq.s_g)  # g_rows x 3072 x 3072 product
     t = time.perf_counter()
     Q.gemm(xg, wq)
-    t_gemm = (time.perf_counter() - t) / (2 * 64 * 3072 * 3072)   # s per FLOP
-    kb, vb = synth.kv_chunk(t=1024)
-    pool = KV.KVPool(1, 24, 128, 256, 4, 1, np.arange(4)[None, :], 4)
+    t_gemm = (time.perf_counter() - t) / (2 * g_rows * 3072 * 3072)   # s per FLOP
+    kb, vb = synth.kv_chunk(t=kv_tok)
+    pool = KV.KVPool(1, 24, 128, 256, kv_pages, 1, np.arange(kv_pages)[None, :], kv_pages)
     t = time.perf_counter()
     pool.write_chunk(0, 0, F.bf16_bits_to_f64(kb), F.bf16_bits_to_f64(vb), 0)
     t_kvw = (time.perf_counter() - t) / kb.size           # per element of K (K and V done)
     t = time.perf_counter()
-    pool.dequant_pages(0, [0, 1, 2, 3])
-    t_kvr = (time.perf_counter() - t) / 4                 # per page
+    pool.dequant_pages(0, list(range(kv_pages)))
+    t_kvr = (time.perf_counter() - t) / kv_pages          # per page
 
     est = {
         "attn_quantize": t_q * 4096 * 3072,
@@ -267,8 +269,9 @@ def cpu_baseline(ops):
         "unit": "% of MI355X roofline (whole step, extrapolated)",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": ("oracle timed on 256x3072 activation rows (quantize, bf16 dequantize), a "
-                   "64x3072x3072 exact GEMM, a 1024-token KV chunk write and 4 KV pages read; "
+        "sample": (f"oracle timed on {q_rows}x3072 activation rows (quantize, bf16 dequantize), a "
+                   f"{g_rows}x3072x3072 exact GEMM, a {kv_tok}-token KV chunk write and "
+                   f"{kv_pages} KV pages read; "
                    "per-unit times scaled to the full step; elementwise numpy is single-"
                    "threaded, the GEMM's fp64 BLAS uses the listed threads"),
         "step_seconds_estimate": step,
