@@ -166,6 +166,59 @@ class KVPool:
         return np.concatenate(outs_k), np.concatenate(outs_v)
 
 
+def window_keys(pool, layer, logical_pages, last_page_tokens, n_phys_pages):
+    """K^, V^ [n, H, D] and the key mask [n] of a listed window.
+
+    Reading (the pages say only that many cache blocks of a time window are
+    decompressed in parallel): a listed page contributes all its slots, except
+    the last listed page, which contributes its first ``last_page_tokens``;
+    a listed page that is not mapped (page table entry outside the pool, or a
+    logical index outside the table) contributes no keys.
+    """
+    P = pool.P
+    keys_k, keys_v, mask = [], [], []
+    for i, lp in enumerate(logical_pages):
+        n_valid = last_page_tokens if i == len(logical_pages) - 1 else P
+        mapped = 0 <= lp < pool.max_pages and 0 <= pool.page_table[layer, lp] < n_phys_pages
+        if mapped:
+            k, v = pool.dequant_pages(layer, [lp])
+        else:
+            k = np.zeros((P, pool.H, pool.D))
+            v = np.zeros((P, pool.H, pool.D))
+        keys_k.append(k)
+        keys_v.append(v)
+        mask.append((np.arange(P) < n_valid) & mapped)
+    return np.concatenate(keys_k), np.concatenate(keys_v), np.concatenate(mask)
+
+
+def attention(pool, layer, logical_pages, last_page_tokens, q, scale, n_phys_pages=None):
+    """Attention of queries q [n_q, H, D] over the valid keys of a listed window.
+
+    O[n, h] = sum_j softmax_j(scale * q[n, h] . K^[j, h]) V^[j, h] over the
+    valid keys j (see window_keys), computed in fp64 (the definition; the
+    device's result is compared within a tolerance).  Reading: every query
+    sees every valid key of the window (no causal mask: the window is the
+    context the new chunk attends to).  No valid key -> O = 0.
+    """
+    if n_phys_pages is None:
+        n_phys_pages = pool.pool.shape[0]
+    k, v, mask = window_keys(pool, layer, logical_pages, last_page_tokens, n_phys_pages)
+    k, v = k[mask], v[mask]
+    n_q, H, D = q.shape
+    out = np.zeros((n_q, H, D))
+    weight_abs_v = np.zeros((n_q, H, D))
+    if k.shape[0] == 0:
+        return out, weight_abs_v
+    for h in range(H):
+        logits = scale * (q[:, h, :] @ k[:, h, :].T)             # [n_q, n_keys]
+        logits -= logits.max(axis=1, keepdims=True)
+        w = np.exp(logits)
+        w /= w.sum(axis=1, keepdims=True)
+        out[:, h, :] = w @ v[:, h, :]
+        weight_abs_v[:, h, :] = w @ np.abs(v[:, h, :])
+    return out, weight_abs_v
+
+
 def _qsb(codes, scales):
     """q * s_b (exact fp64) for [H, P, D/2] codes and [H, P, D/16] scale bytes."""
     h, p, half = codes.shape

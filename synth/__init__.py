@@ -170,3 +170,8 @@ class LongContextKV:
         last = self.pages_per_layer
         recent = recent_tokens // self.P
         return list(range(sink_pages)) + list(range(last - recent, last))
+
+
+def attn_queries(n_q, h=KV_HEADS, d=KV_HEAD_DIM, seed=50, std=1.0) -> np.ndarray:
+    """Queries [n_q, h, d] as bf16 bits (normal, so q.k / sqrt(d) is O(1))."""
+    return to_bf16_bits(normal_f32((n_q, h, d), std, seed))
