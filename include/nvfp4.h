@@ -189,6 +189,32 @@ int nvfp4_kv_dequant_blocks(const nvfp4_kv_cache_t* cache, int32_t layer,
                             const int32_t* logical_pages, int32_t n_pages, void* k_out,
                             void* v_out, void* stream);
 
+/* Attention of new queries over a window of the cache, reading the NVFP4
+ * pages directly: no bf16 K or V is written to memory (techwalker summary,
+ * section 四: the cache is decompressed block by block for the time window;
+ * here each block is decompressed into on-chip memory and consumed at once).
+ * For every query row n and head h:
+ *   O[n][h] = sum_j softmax_j(softmax_scale * q[n][h] . K^[j][h]) V^[j][h]
+ * over the valid keys j of the window, with K^, V^ exactly the values
+ * nvfp4_kv_dequant_blocks produces.  Valid keys: every slot of every listed
+ * logical page, except the last listed page, which contributes its first
+ * last_page_tokens slots; a listed page that is not mapped (logical index or
+ * page table entry out of range) contributes none.  Every query sees every
+ * valid key (no causal mask).  Accumulation in fp32, the softmax weights
+ * enter the P V product rounded to bf16, O is rounded once to bf16; rows
+ * with no valid key are 0.
+ *   logical_pages  device int32[n_pages]
+ *   q_bf16         device bf16 [n_q][n_heads][head_dim], 16-byte aligned
+ *   out_bf16       device bf16 [n_q][n_heads][head_dim], 8-byte aligned
+ * Requires head_dim == 128 and page_tokens % 64 == 0.
+ * Errors: EINVAL (nulls, negative sizes, last_page_tokens outside
+ * [0, page_tokens] when n_pages > 0), ESHAPE (head_dim, page_tokens, layer,
+ * alignment, n_heads > 65535). */
+int nvfp4_kv_attention(const nvfp4_kv_cache_t* cache, int32_t layer,
+                       const int32_t* logical_pages, int32_t n_pages, int32_t last_page_tokens,
+                       const void* q_bf16, int64_t n_q, float softmax_scale, void* out_bf16,
+                       void* stream);
+
 /* Library version and messages. */
 int nvfp4_abi_version(void);
 const char* nvfp4_status_string(int status);

@@ -1,0 +1,107 @@
+"""GPU parity of nvfp4_kv_attention (fused attention over the NVFP4 pages)
+against the oracle's window attention.
+
+The oracle builds its own pool from the same seeded inputs (oracle write
+path) and computes O in fp64.  Tolerance, from the device's arithmetic: the
+logits and sums are fp32 (relative error ~1e-6 here), the softmax weights
+enter the P V product rounded to bf16 (each within 2^-9 relative, so
+|dO| <= 2^-9 sum_j w_j |V^_j|) and O is rounded once to bf16 (2^-9 |O|).  The
+test allows four times the first term and twice the second:
+    |O - O_ref| <= 2^-7 sum_j w_j |V^_j| + 2^-8 |O_ref| + 1e-30.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from helpers import bf16_tensor, dev
+from oracle import formats as F
+from oracle import kvcache as KV
+
+pytestmark = pytest.mark.gpu
+
+import w4a4_gemm_amd as nv  # noqa: E402
+
+
+def _pair(h, p, max_pages, max_chunks, table, n_phys, d=128):
+    gpu = nv.KVCache(1, h, d, p, max_pages, max_chunks, table, n_phys, device=dev())
+    ora = KV.KVPool(1, h, d, p, max_pages, max_chunks, np.asarray(table), n_phys)
+    return gpu, ora
+
+
+def _write(gpu, ora, chunk, kb, vb, start):
+    nv.nvfp4_kv_quantize(gpu, 0, chunk, bf16_tensor(kb), bf16_tensor(vb), start)
+    ora.write_chunk(0, chunk, F.bf16_bits_to_f64(kb), F.bf16_bits_to_f64(vb), start)
+
+
+def _check(gpu, ora, pages, last, qb, scale, n_phys):
+    lp = torch.tensor(pages, dtype=torch.int32, device=dev())
+    out = nv.nvfp4_kv_attention(gpu, 0, lp, last, bf16_tensor(qb), scale)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    ref, wabs = KV.attention(ora, 0, pages, last, F.bf16_bits_to_f64(qb), scale, n_phys)
+    bound = 2.0 ** -7 * wabs + 2.0 ** -8 * np.abs(ref) + 1e-30
+    err = np.abs(o - ref)
+    worst = float(np.max(err / bound))
+    assert worst <= 1.0, f"worst error / bound = {worst}"
+    return worst
+
+
+def test_ragged_queries_partial_last_page():
+    h, p = 3, 64
+    table = np.random.default_rng(3).permutation(8).astype(np.int32)[None, :]
+    gpu, ora = _pair(h, p, 8, 1, table, 8)
+    kb, vb = synth.kv_chunk(t=300, h=h, d=128, seed_k=81, seed_v=82, seed_off=83)
+    _write(gpu, ora, 0, kb, vb, 0)                          # pages 0..4, last holds 44 tokens
+    qb = synth.attn_queries(200, h, 128, seed=84)           # 200 rows: two query blocks, ragged
+    _check(gpu, ora, [0, 1, 2, 3, 4], 300 - 4 * p, qb, 1 / math.sqrt(128), 8)
+
+
+def test_two_chunks_unmapped_page_and_order():
+    h, p = 2, 128
+    table = np.array([[5, 2, 7, 0, -1, 3, 1, 4]], dtype=np.int32)   # logical page 4 unmapped
+    gpu, ora = _pair(h, p, 8, 2, table, 8)
+    kb, vb = synth.kv_chunk(t=600, h=h, d=128, seed_k=85, seed_v=86, seed_off=87)
+    _write(gpu, ora, 0, kb[:200], vb[:200], 0)              # chunk 0: pages 0, 1 (72 slots)
+    _write(gpu, ora, 1, kb[200:500], vb[200:500], 200)      # chunk 1: rest of page 1, 2, 3 (116)
+    qb = synth.attn_queries(130, h, 128, seed=88)
+    # page 1 holds both chunks; page 4 is unmapped and contributes nothing
+    _check(gpu, ora, [3, 1, 4, 0, 2], 128, qb, 0.09, 8)
+    _check(gpu, ora, [1, 0, 3], 500 - 3 * p, qb, 0.09, 8)
+
+
+def test_single_key_and_empty_window():
+    h, p = 1, 64
+    gpu, ora = _pair(h, p, 2, 1, np.array([[1, 0]], dtype=np.int32), 2)
+    kb, vb = synth.kv_chunk(t=64, h=h, d=128, seed_k=89, seed_v=90, seed_off=91)
+    _write(gpu, ora, 0, kb, vb, 0)
+    qb = synth.attn_queries(5, h, 128, seed=92)
+    _check(gpu, ora, [0], 1, qb, 0.5, 2)                    # one key: O = V^[0] up to rounding
+    lp = torch.zeros(0, dtype=torch.int32, device=dev())
+    out = nv.nvfp4_kv_attention(gpu, 0, lp, 0, bf16_tensor(qb), 0.5)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0            # no valid key -> 0
+
+
+def test_large_logits_stay_finite():
+    # sharp softmax: queries scaled up so logits reach a few hundred
+    h, p = 2, 64
+    gpu, ora = _pair(h, p, 4, 1, np.arange(4, dtype=np.int32)[None, :], 4)
+    kb, vb = synth.kv_chunk(t=256, h=h, d=128, seed_k=93, seed_v=94, seed_off=95)
+    _write(gpu, ora, 0, kb, vb, 0)
+    qb = synth.attn_queries(64, h, 128, seed=96, std=8.0)
+    _check(gpu, ora, [0, 1, 2, 3], 64, qb, 1 / math.sqrt(128), 4)
+
+
+def test_dit_heads_window_of_the_written_chunk():
+    # 24 heads x 128, 256-token pages: a 7040-token chunk and 160 of its queries
+    h, p = 24, 256
+    table = synth.page_permutation(28, 33)[None, :]
+    gpu, ora = _pair(h, p, 28, 1, table, 28)
+    kb, vb = synth.kv_chunk()
+    _write(gpu, ora, 0, kb, vb, 0)
+    qb = synth.attn_queries(160, h, 128, seed=97)
+    _check(gpu, ora, list(range(28)), 7040 - 27 * p, qb, 1 / math.sqrt(128), 28)

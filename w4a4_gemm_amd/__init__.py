@@ -20,7 +20,7 @@ __all__ = [
     "NVFP4Tensor", "KVCache", "LIB_PATH",
     "nvfp4_abi_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_kv_page_bytes",
     "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm_w4a4",
-    "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks",
+    "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks", "nvfp4_kv_attention",
     "SCALES_ROWMAJOR", "SCALES_TILED", "OP_QUANTIZE", "OP_KV_QUANTIZE",
 ]
 
@@ -36,7 +36,7 @@ ABI_VERSION = 1
 EXPORTS = (
     "nvfp4_abi_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_kv_page_bytes",
     "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm_w4a4",
-    "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks",
+    "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks", "nvfp4_kv_attention",
 )
 
 
@@ -77,6 +77,8 @@ def _load():
                                              vp, sz, vp]),
         "nvfp4_kv_dequant_blocks": (ctypes.c_int, [ctypes.POINTER(_KVCache), i32, vp, i32, vp, vp,
                                                    vp]),
+        "nvfp4_kv_attention": (ctypes.c_int, [ctypes.POINTER(_KVCache), i32, vp, i32, i32, vp, i64,
+                                              ctypes.c_float, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)            # AttributeError if the symbol is missing
@@ -257,3 +259,20 @@ def nvfp4_kv_dequant_blocks(cache, layer, logical_pages, k_out=None, v_out=None,
                                       _ptr(k_out), _ptr(v_out), _stream(stream))
     _check(st, "nvfp4_kv_dequant_blocks")
     return k_out, v_out
+
+
+def nvfp4_kv_attention(cache, layer, logical_pages, last_page_tokens, q, softmax_scale,
+                       out=None, stream=None):
+    """Attention of q bf16 [n_q, H, D] over the listed window, read from the NVFP4 pages."""
+    if q.dtype != torch.bfloat16 or not q.is_contiguous():
+        raise TypeError("q must be contiguous bf16 [n_q, n_heads, head_dim]")
+    if tuple(q.shape[1:]) != (cache.n_heads, cache.head_dim):
+        raise ValueError("q must be [n_q, n_heads, head_dim]")
+    if out is None:
+        out = torch.empty_like(q)
+    n = logical_pages.numel()
+    st = _lib.nvfp4_kv_attention(ctypes.byref(cache.c()), layer, _ptr(logical_pages), n,
+                                 last_page_tokens, _ptr(q), q.shape[0], float(softmax_scale),
+                                 _ptr(out), _stream(stream))
+    _check(st, "nvfp4_kv_attention")
+    return out

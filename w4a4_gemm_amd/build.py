@@ -24,7 +24,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnvfp4.so")
-SOURCES = ["capi.cpp", "quant.hip", "kv.hip", "gemm.hip"]
+SOURCES = ["capi.cpp", "quant.hip", "kv.hip", "kv_attn.hip", "gemm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

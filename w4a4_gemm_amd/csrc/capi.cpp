@@ -197,4 +197,26 @@ int nvfp4_kv_dequant_blocks(const nvfp4_kv_cache_t* cache, int32_t layer,
   return finish();
 }
 
+int nvfp4_kv_attention(const nvfp4_kv_cache_t* cache, int32_t layer,
+                       const int32_t* logical_pages, int32_t n_pages, int32_t last_page_tokens,
+                       const void* q_bf16, int64_t n_q, float softmax_scale, void* out_bf16,
+                       void* stream) {
+  nvfp4::KvGeom g;
+  int st = check_cache(cache, layer, &g);
+  if (st) return st;
+  if (cache->head_dim != 128 || cache->page_tokens % 64) return NVFP4_ESHAPE;
+  if (n_pages < 0 || n_q < 0) return NVFP4_EINVAL;
+  if (n_pages > 0 && (last_page_tokens < 0 || last_page_tokens > cache->page_tokens))
+    return NVFP4_EINVAL;
+  if (n_q == 0) return NVFP4_OK;
+  if (!q_bf16 || !out_bf16 || (n_pages > 0 && !logical_pages)) return NVFP4_EINVAL;
+  if (!aligned(q_bf16, 16) || !aligned(out_bf16, 8) || (n_pages > 0 && !aligned(logical_pages, 4)))
+    return NVFP4_ESHAPE;
+  if ((n_q + 127) / 128 >= (int64_t(1) << 31)) return NVFP4_ESHAPE;
+  (void)hipGetLastError();
+  nvfp4::launch_kv_attention(g, logical_pages, n_pages, last_page_tokens, (const uint16_t*)q_bf16,
+                             n_q, softmax_scale, (uint16_t*)out_bf16, as_stream(stream));
+  return finish();
+}
+
 }  // extern "C"

@@ -313,37 +313,13 @@ struct UnitPtrs {
   int64_t c_stride, s_stride;          // bytes per token (row) in the codes / scale regions
 };
 
-// One token of one unit: 8 K and 8 V values.
+// One token of one unit: 8 K and 8 V values, stored as 16 bytes each.
 template <bool kVCheck>
 __device__ __forceinline__ void dequant_unit(uint32_t kcw, uint32_t ksb, uint32_t vcw,
                                              uint32_t vsb, float sgk, float sgv, const float* mu,
                                              uint16_t* ko_p, uint16_t* vo_p) {
-  const float sbk = e4m3_value(ksb), sbv = e4m3_value(vsb);
-  float ka[8], kf[8], vf[8];
-  uint32_t off = 0xFFFFFFFFu;
-#pragma unroll
-  for (int sel = 0; sel < 4; ++sel) {
-    const f32x2 qk = e2m1_pair(kcw, sel);
-    const f32x2 qv = e2m1_pair(vcw, sel);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int n = 2 * sel + e;
-      ka[n] = qk[e] * sbk;                                  // exact
-      kf[n] = __builtin_fmaf(ka[n], sgk, mu[n]);
-      off = min(off, off_midpoint(kf[n]));
-      vf[n] = kVCheck ? mul_for_bf16(qv[e] * sbv, sgv) : (qv[e] * sbv) * sgv;
-    }
-  }
-  if (__builtin_expect(off == 0u, 0)) {
-#pragma unroll
-    for (int n = 0; n < 8; ++n) kf[n] = fma_for_bf16(ka[n], sgk, mu[n]);
-  }
   u32x4 ko, vo;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    ko[q] = pack_bf16x2(kf[2 * q], kf[2 * q + 1]);
-    vo[q] = pack_bf16x2(vf[2 * q], vf[2 * q + 1]);
-  }
+  kv_unit_bf16<kVCheck>(kcw, ksb, vcw, vsb, sgk, sgv, mu, ko, vo);
   *(u32x4*)ko_p = ko;
   *(u32x4*)vo_p = vo;
 }

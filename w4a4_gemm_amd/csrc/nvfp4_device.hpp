@@ -274,6 +274,46 @@ __device__ __forceinline__ float fma_for_bf16(float a, float g, float mu) {
   return f;
 }
 
+// ------------------------------------------------------------------ KV decode
+
+// One (token, head) unit of the paged KV cache: 8 codes of K and of V (one
+// dword each) and their scale bytes -> K^ = RN_bf16(q s_b s_gK + mu) and
+// V^ = RN_bf16(q s_b s_gV) with one rounding each, as 4 dwords of bf16 pairs.
+// V: RN32(a s_gV) can land on a bf16 midpoint only for the s_gV that
+// product_needs_check() flags (kVCheck, decided per scale); K: the eight fp32
+// FMA results are tested together and the exact slow path runs only when one
+// of them is a bf16 midpoint.
+template <bool kVCheck>
+__device__ __forceinline__ void kv_unit_bf16(uint32_t kcw, uint32_t ksb, uint32_t vcw, uint32_t vsb,
+                                             float sgk, float sgv, const float* mu, u32x4& ko,
+                                             u32x4& vo) {
+  const float sbk = e4m3_value(ksb), sbv = e4m3_value(vsb);
+  float ka[8], kf[8], vf[8];
+  uint32_t off = 0xFFFFFFFFu;
+#pragma unroll
+  for (int sel = 0; sel < 4; ++sel) {
+    const f32x2 qk = e2m1_pair(kcw, sel);
+    const f32x2 qv = e2m1_pair(vcw, sel);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int n = 2 * sel + e;
+      ka[n] = qk[e] * sbk;                                  // exact
+      kf[n] = __builtin_fmaf(ka[n], sgk, mu[n]);
+      off = min(off, off_midpoint(kf[n]));
+      vf[n] = kVCheck ? mul_for_bf16(qv[e] * sbv, sgv) : (qv[e] * sbv) * sgv;
+    }
+  }
+  if (__builtin_expect(off == 0u, 0)) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) kf[n] = fma_for_bf16(ka[n], sgk, mu[n]);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    ko[q] = pack_bf16x2(kf[2 * q], kf[2 * q + 1]);
+    vo[q] = pack_bf16x2(vf[2 * q], vf[2 * q + 1]);
+  }
+}
+
 // ------------------------------------------------------------------ reductions
 
 // max(v, v of lane ^ 1): the two lanes of a 16-value block (DPP quad_perm 1,0,3,2).
