@@ -53,6 +53,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_gemm1_hbm_traffic.md")
 METRIC = "W4A4 GEMM TFLOPS + quant/dequant/KV GB/s, as % of MI355X roofline"
 
 NV_ELEM = 0.5625               # NVFP4 bytes per element (4-bit code + E4M3 per 16)
+ATTN_QUERIES = 880             # one latent frame of queries for the fused window attention
 
 
 # ------------------------------------------------------------------ workload accounting
@@ -78,6 +79,13 @@ def op_table():
         "kv_read": {"bytes": layers * (win_pages * page_bytes + 2 * win_elems * 2),
                     "compressed_bytes": layers * win_pages * page_bytes},
     }
+
+
+def next_op_table():
+    """Algorithmic work of the rows measured beside the step."""
+    keys = 68 * 256
+    return {"kv_attention": {"flops": 4 * ATTN_QUERIES * keys * 128 * 24,
+                             "compressed_bytes": 68 * 2 * 24 * 256 * (64 + 8)}}
 
 
 def roofline_seconds(op):
@@ -140,6 +148,11 @@ class Workload:
         n = self.window.numel() * r.P
         self.kh = torch.empty((n, r.H, r.D), dtype=torch.bfloat16, device=dev)
         self.vh = torch.empty((n, r.H, r.D), dtype=torch.bfloat16, device=dev)
+        # next row (not part of the step): one 880-token latent frame's queries
+        # attending to layer 0's window, read straight from the NVFP4 pages
+        self.attn_q = bf16(synth.attn_queries(ATTN_QUERIES, r.H, r.D, seed=50))
+        self.attn_out = torch.empty_like(self.attn_q)
+        self.attn_last = r.P
         self._ops = self.ops()
         torch.cuda.synchronize()
 
@@ -170,6 +183,13 @@ class Workload:
                                                       workspace=self.kv_ws)),
             ("kv_read", kv_read),
         ]
+
+    def next_ops(self):
+        """Rows built beyond the step, measured on their own."""
+        nv = self.nv
+        return [("kv_attention", lambda: nv.nvfp4_kv_attention(
+            self.lc, 0, self.window, self.attn_last, self.attn_q, 1.0 / 128 ** 0.5,
+            out=self.attn_out))]
 
     def step(self, ev=None):
         """One pass of the hot path.  ``ev(name)`` records a timing event boundary."""
@@ -210,7 +230,18 @@ def run_gpu(steps, warmup):
         for (n, a), (_, b) in zip(evs[:-1], evs[1:]):
             acc[n] += a.elapsed_time(b) * 1e-3
     per_op = {n: acc[n] / steps for n in names}
-    return wall, per_op
+    nxt = {}
+    for n, fn in wl.next_ops():
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        nxt[n] = a.elapsed_time(b) * 1e-3 / steps
+    return wall, per_op, nxt
 
 
 # ------------------------------------------------------------------ CPU oracle baseline
@@ -305,7 +336,7 @@ def measured_traffic():
 def run_only(name, reps, warmup):
     import torch
     wl = Workload(torch.device("cuda", 0))
-    fn = dict(wl.ops())[name]
+    fn = dict(wl.ops() + wl.next_ops())[name]
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -351,7 +382,7 @@ def main():
         return
 
     ops = op_table()
-    wall, per_op = run_gpu(args.steps, args.warmup)
+    wall, per_op, nxt = run_gpu(args.steps, args.warmup)
     roof = sum(roofline_seconds(o) for o in ops.values())
 
     per = {}
@@ -365,6 +396,15 @@ def main():
         if "compressed_bytes" in o:
             rec["gbps_compressed_read"] = round(o["compressed_bytes"] / s / 1e9, 1)
         per[n] = rec
+
+    nxt_rec = {}
+    for n, o in next_op_table().items():
+        t = nxt[n]
+        nxt_rec[n] = {"ms": round(t * 1e3, 4), "tflops": round(o["flops"] / t / 1e12, 2),
+                      "roofline_frac": round(o["flops"] / t / MFMA_F16_FLOPS, 4),
+                      "workload": (f"{ATTN_QUERIES} queries x 24 heads x 128 over a 68-page "
+                                   "window (17408 keys), pages read as NVFP4; bf16 MFMA"),
+                      "in_step": False}
 
     g1 = per_op["ffn_gemm1"]
     line = {
@@ -396,6 +436,7 @@ def main():
             "traffic": measured_traffic(),
         },
         "per_op": per,
+        "next_ops": nxt_rec,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(ops)

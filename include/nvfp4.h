@@ -79,11 +79,17 @@ typedef struct {
 } nvfp4_tensor_t;
 
 /* Operation ids for nvfp4_workspace_bytes. */
-typedef enum { NVFP4_OP_QUANTIZE = 0, NVFP4_OP_KV_QUANTIZE = 1 } nvfp4_op_t;
+typedef enum {
+  NVFP4_OP_QUANTIZE = 0,
+  NVFP4_OP_KV_QUANTIZE = 1,
+  NVFP4_OP_KV_ATTENTION = 2
+} nvfp4_op_t;
 
 /* Workspace (device bytes) a call needs.
  *   NVFP4_OP_QUANTIZE:     a = rows, b = cols, c = 1 if the caller passes amax, else 0
  *   NVFP4_OP_KV_QUANTIZE:  a = T (tokens), b = n_heads, c = head_dim
+ *   NVFP4_OP_KV_ATTENTION: a = n_q, b = n_heads, c = n_pages * page_tokens
+ *                          (0 when the window is not split over workgroups)
  * Returns 0 for a bad op id.  The workspace must be 256-byte aligned. */
 size_t nvfp4_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c);
 
@@ -206,14 +212,18 @@ int nvfp4_kv_dequant_blocks(const nvfp4_kv_cache_t* cache, int32_t layer,
  *   logical_pages  device int32[n_pages]
  *   q_bf16         device bf16 [n_q][n_heads][head_dim], 16-byte aligned
  *   out_bf16       device bf16 [n_q][n_heads][head_dim], 8-byte aligned
+ *   workspace      nvfp4_workspace_bytes(NVFP4_OP_KV_ATTENTION, n_q, n_heads,
+ *                  n_pages * page_tokens) bytes, 256-byte aligned: when few
+ *                  (query block, head) pairs exist the window is split over
+ *                  workgroups and their partial results meet there
  * Requires head_dim == 128 and page_tokens % 64 == 0.
  * Errors: EINVAL (nulls, negative sizes, last_page_tokens outside
  * [0, page_tokens] when n_pages > 0), ESHAPE (head_dim, page_tokens, layer,
- * alignment, n_heads > 65535). */
+ * alignment, n_heads > 65535), EWORKSPACE. */
 int nvfp4_kv_attention(const nvfp4_kv_cache_t* cache, int32_t layer,
                        const int32_t* logical_pages, int32_t n_pages, int32_t last_page_tokens,
                        const void* q_bf16, int64_t n_q, float softmax_scale, void* out_bf16,
-                       void* stream);
+                       void* workspace, size_t ws_bytes, void* stream);
 
 /* Library version and messages. */
 int nvfp4_abi_version(void);

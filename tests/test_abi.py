@@ -124,18 +124,24 @@ def test_kv_attention_argument_errors():
     C = nv._KVCache
     good = C(256, 28, 1, 24, 128, 256, 28, 2, 16, 16, 16, 16, 16)
     # nothing to do: no query rows
-    assert lib.nvfp4_kv_attention(ctypes.byref(good), 0, 16, 4, 256, 16, 0, 0.1, 16, None) == nv.OK
+    assert lib.nvfp4_kv_attention(ctypes.byref(good), 0, 16, 4, 256, 16, 0, 0.1, 16, None, 0, None) == nv.OK
     # head_dim other than 128, page_tokens not a multiple of 64
     d64 = C(256, 28, 1, 24, 64, 256, 28, 2, 16, 16, 16, 16, 16)
-    assert lib.nvfp4_kv_attention(ctypes.byref(d64), 0, 16, 4, 256, 16, 8, 0.1, 16, None) == nv.ESHAPE
+    assert lib.nvfp4_kv_attention(ctypes.byref(d64), 0, 16, 4, 256, 16, 8, 0.1, 16, None, 0, None) == nv.ESHAPE
     p100 = C(256, 28, 1, 24, 128, 100, 28, 2, 16, 16, 16, 16, 16)
-    assert lib.nvfp4_kv_attention(ctypes.byref(p100), 0, 16, 4, 100, 16, 8, 0.1, 16, None) == nv.ESHAPE
+    assert lib.nvfp4_kv_attention(ctypes.byref(p100), 0, 16, 4, 100, 16, 8, 0.1, 16, None, 0, None) == nv.ESHAPE
     # last page token count out of range, negative sizes, null query / output
-    assert lib.nvfp4_kv_attention(ctypes.byref(good), 0, 16, 4, 257, 16, 8, 0.1, 16, None) == nv.EINVAL
-    assert lib.nvfp4_kv_attention(ctypes.byref(good), 0, 16, -1, 0, 16, 8, 0.1, 16, None) == nv.EINVAL
-    assert lib.nvfp4_kv_attention(ctypes.byref(good), 0, 16, 4, 256, 16, -8, 0.1, 16, None) == nv.EINVAL
-    assert lib.nvfp4_kv_attention(ctypes.byref(good), 0, 16, 4, 256, None, 8, 0.1, 16, None) == nv.EINVAL
-    assert lib.nvfp4_kv_attention(ctypes.byref(good), 0, 16, 4, 256, 16, 8, 0.1, None, None) == nv.EINVAL
+    assert lib.nvfp4_kv_attention(ctypes.byref(good), 0, 16, 4, 257, 16, 8, 0.1, 16, None, 0, None) == nv.EINVAL
+    assert lib.nvfp4_kv_attention(ctypes.byref(good), 0, 16, -1, 0, 16, 8, 0.1, 16, None, 0, None) == nv.EINVAL
+    assert lib.nvfp4_kv_attention(ctypes.byref(good), 0, 16, 4, 256, 16, -8, 0.1, 16, None, 0, None) == nv.EINVAL
+    assert lib.nvfp4_kv_attention(ctypes.byref(good), 0, 16, 4, 256, None, 8, 0.1, 16, None, 0, None) == nv.EINVAL
+    assert lib.nvfp4_kv_attention(ctypes.byref(good), 0, 16, 4, 256, 16, 8, 0.1, None, None, 0, None) == nv.EINVAL
     # misaligned query rows, layer out of range
-    assert lib.nvfp4_kv_attention(ctypes.byref(good), 0, 16, 4, 256, 18, 8, 0.1, 16, None) == nv.ESHAPE
-    assert lib.nvfp4_kv_attention(ctypes.byref(good), 1, 16, 4, 256, 16, 8, 0.1, 16, None) == nv.ESHAPE
+    assert lib.nvfp4_kv_attention(ctypes.byref(good), 0, 16, 4, 256, 18, 8, 0.1, 16, None, 0, None) == nv.ESHAPE
+    assert lib.nvfp4_kv_attention(ctypes.byref(good), 1, 16, 4, 256, 16, 8, 0.1, 16, None, 0, None) == nv.ESHAPE
+    # a small grid splits the window over workgroups: the workspace is then required
+    need = nv.nvfp4_workspace_bytes(nv.OP_KV_ATTENTION, 100, 24, 68 * 256)
+    assert need > 0
+    assert nv.nvfp4_workspace_bytes(nv.OP_KV_ATTENTION, 7040, 24, 68 * 256) == 0
+    assert lib.nvfp4_kv_attention(ctypes.byref(good), 0, 16, 68, 256, 16, 100, 0.1, 16, None, 0,
+                                  None) == nv.EWORKSPACE

@@ -105,3 +105,16 @@ def test_dit_heads_window_of_the_written_chunk():
     _write(gpu, ora, 0, kb, vb, 0)
     qb = synth.attn_queries(160, h, 128, seed=97)
     _check(gpu, ora, list(range(28)), 7040 - 27 * p, qb, 1 / math.sqrt(128), 28)
+
+
+def test_split_window_with_an_empty_split():
+    # 20 blocks for a 1-block query grid: the window is split over workgroups,
+    # and the first half of the listed pages is unmapped (that split sees no key)
+    h, p = 2, 64
+    table = np.array([[-1] * 10 + list(range(10))], dtype=np.int32)
+    gpu, ora = _pair(h, p, 20, 1, table, 10)
+    assert nv.nvfp4_workspace_bytes(nv.OP_KV_ATTENTION, 50, h, 20 * p) > 0
+    kb, vb = synth.kv_chunk(t=10 * p, h=h, d=128, seed_k=98, seed_v=99, seed_off=100)
+    _write(gpu, ora, 0, kb, vb, 10 * p)                     # logical pages 10..19
+    qb = synth.attn_queries(50, h, 128, seed=101)
+    _check(gpu, ora, list(range(20)), p, qb, 1 / math.sqrt(128), 10)

@@ -21,7 +21,7 @@ __all__ = [
     "nvfp4_abi_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_kv_page_bytes",
     "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm_w4a4",
     "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks", "nvfp4_kv_attention",
-    "SCALES_ROWMAJOR", "SCALES_TILED", "OP_QUANTIZE", "OP_KV_QUANTIZE",
+    "SCALES_ROWMAJOR", "SCALES_TILED", "OP_QUANTIZE", "OP_KV_QUANTIZE", "OP_KV_ATTENTION",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so")
@@ -30,7 +30,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so
 OK, EINVAL, ESHAPE, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 SCALES_ROWMAJOR, SCALES_TILED = 0, 1
-OP_QUANTIZE, OP_KV_QUANTIZE = 0, 1
+OP_QUANTIZE, OP_KV_QUANTIZE, OP_KV_ATTENTION = 0, 1, 2
 ABI_VERSION = 1
 
 EXPORTS = (
@@ -78,7 +78,7 @@ def _load():
         "nvfp4_kv_dequant_blocks": (ctypes.c_int, [ctypes.POINTER(_KVCache), i32, vp, i32, vp, vp,
                                                    vp]),
         "nvfp4_kv_attention": (ctypes.c_int, [ctypes.POINTER(_KVCache), i32, vp, i32, i32, vp, i64,
-                                              ctypes.c_float, vp, vp]),
+                                              ctypes.c_float, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)            # AttributeError if the symbol is missing
@@ -262,7 +262,7 @@ def nvfp4_kv_dequant_blocks(cache, layer, logical_pages, k_out=None, v_out=None,
 
 
 def nvfp4_kv_attention(cache, layer, logical_pages, last_page_tokens, q, softmax_scale,
-                       out=None, stream=None):
+                       out=None, workspace=None, stream=None):
     """Attention of q bf16 [n_q, H, D] over the listed window, read from the NVFP4 pages."""
     if q.dtype != torch.bfloat16 or not q.is_contiguous():
         raise TypeError("q must be contiguous bf16 [n_q, n_heads, head_dim]")
@@ -271,8 +271,13 @@ def nvfp4_kv_attention(cache, layer, logical_pages, last_page_tokens, q, softmax
     if out is None:
         out = torch.empty_like(q)
     n = logical_pages.numel()
+    need = nvfp4_workspace_bytes(OP_KV_ATTENTION, q.shape[0], cache.n_heads, n * cache.page_tokens)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     st = _lib.nvfp4_kv_attention(ctypes.byref(cache.c()), layer, _ptr(logical_pages), n,
                                  last_page_tokens, _ptr(q), q.shape[0], float(softmax_scale),
-                                 _ptr(out), _stream(stream))
+                                 _ptr(out), _ptr(workspace),
+                                 workspace.numel() if workspace is not None else 0,
+                                 _stream(stream))
     _check(st, "nvfp4_kv_attention")
     return out

@@ -62,6 +62,8 @@ size_t nvfp4_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c) {
   switch (op) {
     case NVFP4_OP_QUANTIZE: return nvfp4::quantize_workspace_bytes(a, b, c != 0);
     case NVFP4_OP_KV_QUANTIZE: return nvfp4::kv_quantize_workspace_bytes(a, b, c);
+    case NVFP4_OP_KV_ATTENTION:
+      return a < 0 || b <= 0 || c < 0 ? 0 : nvfp4::kv_attention_workspace_bytes(a, b, c);
     default: return 0;
   }
 }
@@ -200,7 +202,7 @@ int nvfp4_kv_dequant_blocks(const nvfp4_kv_cache_t* cache, int32_t layer,
 int nvfp4_kv_attention(const nvfp4_kv_cache_t* cache, int32_t layer,
                        const int32_t* logical_pages, int32_t n_pages, int32_t last_page_tokens,
                        const void* q_bf16, int64_t n_q, float softmax_scale, void* out_bf16,
-                       void* stream) {
+                       void* workspace, size_t ws_bytes, void* stream) {
   nvfp4::KvGeom g;
   int st = check_cache(cache, layer, &g);
   if (st) return st;
@@ -213,9 +215,13 @@ int nvfp4_kv_attention(const nvfp4_kv_cache_t* cache, int32_t layer,
   if (!aligned(q_bf16, 16) || !aligned(out_bf16, 8) || (n_pages > 0 && !aligned(logical_pages, 4)))
     return NVFP4_ESHAPE;
   if ((n_q + 127) / 128 >= (int64_t(1) << 31)) return NVFP4_ESHAPE;
+  const size_t need = nvfp4::kv_attention_workspace_bytes(
+      n_q, cache->n_heads, (int64_t)n_pages * cache->page_tokens);
+  if (need && (!workspace || ws_bytes < need || !aligned(workspace, 256))) return NVFP4_EWORKSPACE;
   (void)hipGetLastError();
   nvfp4::launch_kv_attention(g, logical_pages, n_pages, last_page_tokens, (const uint16_t*)q_bf16,
-                             n_q, softmax_scale, (uint16_t*)out_bf16, as_stream(stream));
+                             n_q, softmax_scale, (uint16_t*)out_bf16, workspace,
+                             as_stream(stream));
   return finish();
 }
 

@@ -40,12 +40,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 
 // Per-page facts, uniform over the workgroup.
 struct PageInfo {
-  const uint8_t* page;    // null when the page is not mapped
+  const uint8_t* page;    // a valid page address (page 0 when unmapped: loads stay in bounds)
+  bool mapped;
   int valid;              // valid slots of the page (keys beyond are masked)
   int split;              // slots [0, split) belong to chunk c0, the rest to c1
   int c0, c1;
   float sgk0, sgk1, sgv0, sgv1;
-  bool vcheck;            // some V product of this page may need the midpoint fix-up
 };
 
 __device__ __forceinline__ PageInfo page_info(const KvGeom& g, int64_t n_phys,
@@ -56,7 +56,8 @@ __device__ __forceinline__ PageInfo page_info(const KvGeom& g, int64_t n_phys,
   bool mapped = lp >= 0 && lp < g.max_pages;
   const int64_t phys = mapped ? (int64_t)g.page_table[lp] : -1;
   mapped = mapped && phys >= 0 && phys < n_phys;
-  p.page = mapped ? g.pool + phys * g.page_bytes : nullptr;
+  p.mapped = mapped;
+  p.page = g.pool + (mapped ? phys : 0) * g.page_bytes;
   p.valid = !mapped ? 0 : (pi == n_pages - 1 ? last_tokens : g.page_tokens);
   int c0 = mapped ? g.page_chunk[2 * lp] : 0;
   p.split = mapped ? g.page_chunk[2 * lp + 1] : g.page_tokens;
@@ -67,63 +68,118 @@ __device__ __forceinline__ PageInfo page_info(const KvGeom& g, int64_t n_phys,
   p.sgk1 = g.k_gscale[p.c1];
   p.sgv0 = g.v_gscale[p.c0];
   p.sgv1 = g.v_gscale[p.c1];
-  p.vcheck = product_needs_check(p.sgv0) || product_needs_check(p.sgv1);
   return p;
 }
 
-// Decode keys [s0, s0 + 64) of head h of one page into K^ rows and V^T
-// columns of LDS.  Thread t handles units t + 256 i (i = 0..3): key u / 16,
-// channel group u % 16 (8 channels).
-__device__ __forceinline__ void decode_block(const KvGeom& g, const PageInfo& p, int h, int s0,
-                                             uint16_t* __restrict__ Ks,
-                                             uint16_t* __restrict__ Vt) {
+// The raw inputs of one block for this thread: its units are the 4 adjacent
+// keys 4 (tid / 16) + i (i = 0..3) in channel group tid % 16 (the same 8
+// channels for every unit), so the thread needs the K means of those 8
+// channels for the page's two chunks, and writes V^T as 4-key runs.
+struct BlockRaw {
+  uint32_t kc[4], ks[4], vc[4], vs[4];
+  f32x4 mu0a, mu0b, mu1a, mu1b;
+};
+
+__device__ __forceinline__ void fetch_block(const KvGeom& g, const PageInfo& p, int h, int s0,
+                                            BlockRaw& r) {
   const int H = g.n_heads, P = g.page_tokens;
   const int64_t codes_region = (int64_t)H * P * (kD / 2);
   const int64_t scales_region = (int64_t)H * P * (kD / 16);
+  const int sub = threadIdx.x & 15;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int u = threadIdx.x + 256 * i;
-    const int key = u >> 4, sub = u & 15;
-    const int slot = s0 + key;
-    u32x4 ko = u32x4{0, 0, 0, 0}, vo = u32x4{0, 0, 0, 0};
-    if (p.page) {
-      const int64_t row = (int64_t)h * P + slot;
-      const uint32_t kcw = *(const uint32_t*)(p.page + row * (kD / 2) + 4 * sub);
-      const uint32_t ksb = p.page[codes_region + row * (kD / 16) + (sub >> 1)];
-      const uint32_t vcw =
-          *(const uint32_t*)(p.page + codes_region + scales_region + row * (kD / 2) + 4 * sub);
-      const uint32_t vsb =
-          p.page[2 * codes_region + scales_region + row * (kD / 16) + (sub >> 1)];
-      const bool second = slot >= p.split;
-      const int c = second ? p.c1 : p.c0;
-      const float* mp = g.k_mean + ((int64_t)c * H + h) * kD + 8 * sub;
-      const f32x4 m0 = *(const f32x4*)mp, m1 = *(const f32x4*)(mp + 4);
-      const float mu[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
-      const float sgk = second ? p.sgk1 : p.sgk0, sgv = second ? p.sgv1 : p.sgv0;
-      if (p.vcheck) kv_unit_bf16<true>(kcw, ksb, vcw, vsb, sgk, sgv, mu, ko, vo);
-      else kv_unit_bf16<false>(kcw, ksb, vcw, vsb, sgk, sgv, mu, ko, vo);
+    const int key = 4 * (threadIdx.x >> 4) + i;
+    const int64_t row = (int64_t)h * P + s0 + key;
+    r.kc[i] = *(const uint32_t*)(p.page + row * (kD / 2) + 4 * sub);
+    r.ks[i] = p.page[codes_region + row * (kD / 16) + (sub >> 1)];
+    r.vc[i] = *(const uint32_t*)(p.page + codes_region + scales_region + row * (kD / 2) + 4 * sub);
+    r.vs[i] = p.page[2 * codes_region + scales_region + row * (kD / 16) + (sub >> 1)];
+  }
+  const float* m0 = g.k_mean + ((int64_t)p.c0 * H + h) * kD + 8 * sub;
+  const float* m1 = g.k_mean + ((int64_t)p.c1 * H + h) * kD + 8 * sub;
+  r.mu0a = *(const f32x4*)m0;
+  r.mu0b = *(const f32x4*)(m0 + 4);
+  r.mu1a = *(const f32x4*)m1;
+  r.mu1b = *(const f32x4*)(m1 + 4);
+}
+
+// Decode a fetched block into K^ rows and V^T columns of LDS (unmapped pages
+// give zeros; such keys are masked anyway).
+template <bool kVCheck>
+__device__ __forceinline__ void decode_block(const PageInfo& p, int s0, const BlockRaw& r,
+                                             uint16_t* __restrict__ Ks,
+                                             uint16_t* __restrict__ Vt) {
+  const int sub = threadIdx.x & 15;
+  const float mu0[8] = {r.mu0a[0], r.mu0a[1], r.mu0a[2], r.mu0a[3],
+                        r.mu0b[0], r.mu0b[1], r.mu0b[2], r.mu0b[3]};
+  const float mu1[8] = {r.mu1a[0], r.mu1a[1], r.mu1a[2], r.mu1a[3],
+                        r.mu1b[0], r.mu1b[1], r.mu1b[2], r.mu1b[3]};
+  uint32_t vw[4][4];                                        // V^ words of the 4 keys
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = 4 * (threadIdx.x >> 4) + i;
+    const bool second = s0 + key >= p.split;
+    u32x4 ko, vo;
+    kv_unit_bf16<kVCheck>(r.kc[i], r.ks[i], r.vc[i], r.vs[i], second ? p.sgk1 : p.sgk0,
+                          second ? p.sgv1 : p.sgv0, second ? mu1 : mu0, ko, vo);
+    if (!p.mapped) {
+      ko = u32x4{0, 0, 0, 0};
+      vo = u32x4{0, 0, 0, 0};
     }
     *(u32x4*)(Ks + key * kKsRow + 8 * sub) = ko;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      Vt[(8 * sub + 2 * e) * kVtRow + key] = (uint16_t)(vo[e] & 0xFFFFu);
-      Vt[(8 * sub + 2 * e + 1) * kVtRow + key] = (uint16_t)(vo[e] >> 16);
-    }
+    for (int e = 0; e < 4; ++e) vw[i][e] = vo[e];
+  }
+  // V^T row 8 sub + c holds channel c of the 4 keys: bf16 of key i is the
+  // low (c even) or high (c odd) half of vw[i][c / 2]
+  const int k0 = 4 * (threadIdx.x >> 4);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+    const uint32_t lo = __builtin_amdgcn_perm(vw[1][c >> 1], vw[0][c >> 1], sel);
+    const uint32_t hi = __builtin_amdgcn_perm(vw[3][c >> 1], vw[2][c >> 1], sel);
+    *(u32x2*)(Vt + (8 * sub + c) * kVtRow + k0) = u32x2{lo, hi};
   }
 }
 
 }  // namespace
 
+// Key splits: when the grid of (query block, head) is small, the window is
+// split over several workgroups whose partial results are merged by
+// kv_attention_combine.  A pure function of the sizes, shared by the
+// workspace query and the launcher.
+int attention_splits(int64_t n_q, int64_t n_heads, int64_t n_keys) {
+  const int64_t base = ((n_q + kQB - 1) / kQB) * n_heads;
+  const int64_t blocks = (n_keys + kKB - 1) / kKB;
+  if (base >= 512 || blocks < 16) return 1;
+  int64_t s = (1024 + base - 1) / base;
+  s = s < blocks / 8 ? s : blocks / 8;
+  s = s < 64 ? s : 64;
+  return s < 1 ? 1 : (int)s;
+}
+
+size_t kv_attention_workspace_bytes(int64_t n_q, int64_t n_heads, int64_t n_keys) {
+  const int s = attention_splits(n_q, n_heads, n_keys);
+  if (s == 1) return 0;
+  return (size_t)s * n_q * n_heads * (kD + 2) * sizeof(float);
+}
+
+// Split `split` of `n_split` handles key blocks [b0, b1) of the window.  With
+// one split the result is normalized and written as bf16; otherwise the
+// unnormalized fp32 O^T, the running max m (log2 units) and the sum l go to
+// the workspace: O at part + ((split * n_q + n) * H + h) * D, (m, l) after all
+// O values.
 __global__ __launch_bounds__(256) void kv_attention_kernel(KvGeom g, int64_t n_phys,
                                                            const int32_t* __restrict__ pages,
                                                            int n_pages, int last_tokens,
                                                            const uint16_t* __restrict__ q,
                                                            int64_t n_q, float scale_log2e,
-                                                           uint16_t* __restrict__ out) {
+                                                           uint16_t* __restrict__ out,
+                                                           float* __restrict__ part, int n_split) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kKB * kKsRow];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[kD * kVtRow];
   const int H = g.n_heads, P = g.page_tokens;
-  const int h = blockIdx.y;
+  const int h = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5;
   const int64_t qrow = (int64_t)blockIdx.x * kQB + wave * 32 + (lane & 31);
@@ -145,17 +201,31 @@ __global__ __launch_bounds__(256) void kv_attention_kernel(KvGeom g, int64_t n_p
   float m = -__builtin_inff(), l = 0.0f;
 
   const int bpp = P / kKB;                                  // blocks per page
-  PageInfo pinfo;
-  int cur_page = -1;
-  for (int b = 0; b < n_pages * bpp; ++b) {
-    const int pi = b / bpp, s0 = (b - pi * bpp) * kKB;
-    if (pi != cur_page) {
-      pinfo = page_info(g, n_phys, pages, pi, n_pages, last_tokens);
-      cur_page = pi;
+  const int nb = n_pages * bpp;
+  const int b0 = (int)((int64_t)nb * split / n_split), b1 = (int)((int64_t)nb * (split + 1) / n_split);
+
+  // software pipeline: the raw inputs of block b + 1 are in flight while
+  // block b is decoded and consumed
+  PageInfo pn;
+  BlockRaw rn;
+  if (b0 < b1) {
+    pn = page_info(g, n_phys, pages, b0 / bpp, n_pages, last_tokens);
+    fetch_block(g, pn, h, (b0 % bpp) * kKB, rn);
+  }
+  for (int b = b0; b < b1; ++b) {
+    const int s0 = (b % bpp) * kKB;
+    const PageInfo pc = pn;
+    const BlockRaw rc = rn;
+    if (b + 1 < b1) {
+      if ((b + 1) % bpp == 0) pn = page_info(g, n_phys, pages, (b + 1) / bpp, n_pages, last_tokens);
+      fetch_block(g, pn, h, ((b + 1) % bpp) * kKB, rn);
     }
-    if (pinfo.valid <= s0) continue;                        // whole block masked (uniform)
+    if (pc.valid <= s0) continue;                           // whole block masked (uniform)
     __syncthreads();                                        // previous block's LDS reads done
-    decode_block(g, pinfo, h, s0, Ks, Vt);
+    if (product_needs_check(pc.sgv0) || product_needs_check(pc.sgv1))
+      decode_block<true>(pc, s0, rc, Ks, Vt);
+    else
+      decode_block<false>(pc, s0, rc, Ks, Vt);
     __syncthreads();
 
     // S^T tiles: keys 32 kt + (r / 4) * 8 + 4 half + r % 4 of this block, query lane % 32
@@ -177,7 +247,7 @@ __global__ __launch_bounds__(256) void kv_attention_kernel(KvGeom g, int64_t n_p
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 32 * kt + (r >> 2) * 8 + 4 * half + (r & 3);
-        const float t = s0 + key < pinfo.valid ? st[kt][r] * scale_log2e : -__builtin_inff();
+        const float t = s0 + key < pc.valid ? st[kt][r] * scale_log2e : -__builtin_inff();
         st[kt][r] = t;
         mb = fmaxf(mb, t);
       }
@@ -221,28 +291,76 @@ __global__ __launch_bounds__(256) void kv_attention_kernel(KvGeom g, int64_t n_p
     }
   }
 
-  // O = O^T / l, rounded once to bf16; register r of tile dt is channel
-  // 32 dt + (r / 4) * 8 + 4 half + r % 4.
+  // register r of tile dt is channel 32 dt + (r / 4) * 8 + 4 half + r % 4
   if (qrow < n_q) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    uint16_t* op = out + (qrow * H + h) * kD + 4 * half;
+    if (n_split == 1) {
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      uint16_t* op = out + (qrow * H + h) * kD + 4 * half;
 #pragma unroll
-    for (int dt = 0; dt < kD / 32; ++dt)
+      for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        *(u32x2*)(op + 32 * dt + 8 * g4) =
-            u32x2{pack_bf16x2(o[dt][4 * g4] * inv, o[dt][4 * g4 + 1] * inv),
-                  pack_bf16x2(o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv)};
+        for (int g4 = 0; g4 < 4; ++g4)
+          *(u32x2*)(op + 32 * dt + 8 * g4) =
+              u32x2{pack_bf16x2(o[dt][4 * g4] * inv, o[dt][4 * g4 + 1] * inv),
+                    pack_bf16x2(o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv)};
+    } else {
+      float* op = part + (((int64_t)split * n_q + qrow) * H + h) * kD + 4 * half;
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *(f32x4*)(op + 32 * dt + 8 * g4) =
+              f32x4{o[dt][4 * g4], o[dt][4 * g4 + 1], o[dt][4 * g4 + 2], o[dt][4 * g4 + 3]};
+      if (half == 0) {
+        float* ml = part + (int64_t)n_split * n_q * H * kD + (((int64_t)split * n_q + qrow) * H + h) * 2;
+        *(f32x2*)ml = f32x2{m, l};
+      }
+    }
   }
+}
+
+// Merge the splits of one (query, head) row: M = max m_s, L = sum l_s 2^(m_s - M),
+// O = sum O_s 2^(m_s - M) / L, rounded once to bf16.  One wave per row, two
+// channels per lane.
+__global__ __launch_bounds__(256) void kv_attention_combine(const float* __restrict__ part,
+                                                            int n_split, int64_t rows,
+                                                            uint16_t* __restrict__ out) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float* ml = part + (int64_t)n_split * rows * kD;
+  float M = -__builtin_inff();
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, ml[((int64_t)s * rows + row) * 2]);
+  float L = 0.0f, a0 = 0.0f, a1 = 0.0f;
+  if (M != -__builtin_inff()) {
+    for (int s = 0; s < n_split; ++s) {
+      const f32x2 v = *(const f32x2*)(ml + ((int64_t)s * rows + row) * 2);
+      const float w = __builtin_amdgcn_exp2f(v[0] - M);    // 0 for an empty split (m = -inf)
+      const f32x2 os = *(const f32x2*)(part + ((int64_t)s * rows + row) * kD + 2 * lane);
+      L += v[1] * w;
+      a0 += os[0] * w;
+      a1 += os[1] * w;
+    }
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  *(uint32_t*)(out + row * kD + 2 * lane) = pack_bf16x2(a0 * inv, a1 * inv);
 }
 
 void launch_kv_attention(const KvGeom& g, const int32_t* logical_pages, int32_t n_pages,
                          int32_t last_page_tokens, const uint16_t* q, int64_t n_q,
-                         float softmax_scale, uint16_t* out, hipStream_t stream) {
+                         float softmax_scale, uint16_t* out, void* workspace,
+                         hipStream_t stream) {
   const float scale_log2e = (float)((double)softmax_scale * 1.4426950408889634);
-  const dim3 grid((unsigned)((n_q + kQB - 1) / kQB), (unsigned)g.n_heads);
+  const int n_split = attention_splits(n_q, g.n_heads, (int64_t)n_pages * g.page_tokens);
+  const dim3 grid((unsigned)((n_q + kQB - 1) / kQB), (unsigned)g.n_heads, (unsigned)n_split);
   hipLaunchKernelGGL(kv_attention_kernel, grid, dim3(256), 0, stream, g, g.n_phys_pages,
-                     logical_pages, n_pages, last_page_tokens, q, n_q, scale_log2e, out);
+                     logical_pages, n_pages, last_page_tokens, q, n_q, scale_log2e, out,
+                     (float*)workspace, n_split);
+  if (n_split > 1) {
+    const int64_t rows = n_q * g.n_heads;
+    hipLaunchKernelGGL(kv_attention_combine, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                       stream, (const float*)workspace, n_split, rows, out);
+  }
 }
 
 }  // namespace nvfp4

@@ -48,9 +48,12 @@ void launch_kv_quantize(const KvGeom& g, int32_t chunk_id, const uint16_t* k, co
                         int64_t T, int64_t start_token, void* workspace, hipStream_t stream);
 
 // Fused window attention (kv_attn.hip): head_dim 128, page_tokens % 64 == 0.
+int attention_splits(int64_t n_q, int64_t n_heads, int64_t n_keys);
+size_t kv_attention_workspace_bytes(int64_t n_q, int64_t n_heads, int64_t n_keys);
 void launch_kv_attention(const KvGeom& g, const int32_t* logical_pages, int32_t n_pages,
                          int32_t last_page_tokens, const uint16_t* q, int64_t n_q,
-                         float softmax_scale, uint16_t* out, hipStream_t stream);
+                         float softmax_scale, uint16_t* out, void* workspace,
+                         hipStream_t stream);
 
 void launch_kv_dequant(const KvGeom& g, const int32_t* logical_pages, int32_t n_pages,
                        uint16_t* k_out, uint16_t* v_out, hipStream_t stream);
