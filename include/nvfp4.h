@@ -225,6 +225,29 @@ int nvfp4_kv_attention(const nvfp4_kv_cache_t* cache, int32_t layer,
                        const void* q_bf16, int64_t n_q, float softmax_scale, void* out_bf16,
                        void* workspace, size_t ws_bytes, void* stream);
 
+/* Logical page list of a multi-shot sink window (techwalker summary,
+ * section 六: a global sink on the first frames, a shot sink re-bound to the
+ * start of the current shot and kept as two pointers (start, length), both
+ * laid over a sliding window).  The list holds every logical page with at
+ * least one token of
+ *   [0, global_sink_tokens) U [shot_start, shot_start + shot_sink_tokens)
+ *   U [total_tokens - window_tokens, total_tokens),
+ * each range clipped to [0, total_tokens), in increasing order, each page
+ * once (ranges round outward to whole pages).  The count and the valid
+ * tokens of the last listed page, min(page_tokens, total_tokens -
+ * page_tokens * last_page), are computed on the host and returned at once
+ * (0 and 0 for an empty list); the list is written to device memory by a
+ * kernel on `stream`, ready for nvfp4_kv_dequant_blocks / nvfp4_kv_attention.
+ *   pages_dev         device int32[max_pages] (may be NULL when the list is empty)
+ *   n_pages           host out
+ *   last_page_tokens  host out
+ * Errors: EINVAL (null outputs, negative sizes or lengths, page_tokens <= 0),
+ * ESHAPE (list longer than max_pages, or pages past 2^31 - 1). */
+int nvfp4_kv_window_pages(int64_t total_tokens, int32_t page_tokens, int64_t global_sink_tokens,
+                          int64_t shot_start, int64_t shot_sink_tokens, int64_t window_tokens,
+                          int32_t* pages_dev, int32_t max_pages, int32_t* n_pages,
+                          int32_t* last_page_tokens, void* stream);
+
 /* Library version and messages. */
 int nvfp4_abi_version(void);
 const char* nvfp4_status_string(int status);

@@ -145,3 +145,26 @@ def test_kv_attention_argument_errors():
     assert nv.nvfp4_workspace_bytes(nv.OP_KV_ATTENTION, 7040, 24, 68 * 256) == 0
     assert lib.nvfp4_kv_attention(ctypes.byref(good), 0, 16, 68, 256, 16, 100, 0.1, 16, None, 0,
                                   None) == nv.EWORKSPACE
+
+
+def test_window_pages_host_side():
+    import w4a4_gemm_amd as nv
+    lib = nv._lib
+    n, last = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    # empty cache: no list, nothing launched
+    assert lib.nvfp4_kv_window_pages(0, 256, 1024, 0, 0, 16384, None, 0, ctypes.byref(n),
+                                     ctypes.byref(last), None) == nv.OK
+    assert (n.value, last.value) == (0, 0)
+    # the list would not fit: rejected before any launch
+    assert lib.nvfp4_kv_window_pages(65536, 256, 1024, 0, 0, 16384, 16, 67, ctypes.byref(n),
+                                     ctypes.byref(last), None) == nv.ESHAPE
+    # bad sizes and missing outputs
+    assert lib.nvfp4_kv_window_pages(100, 0, 0, 0, 0, 0, 16, 8, ctypes.byref(n),
+                                     ctypes.byref(last), None) == nv.EINVAL
+    assert lib.nvfp4_kv_window_pages(100, 64, -1, 0, 0, 0, 16, 8, ctypes.byref(n),
+                                     ctypes.byref(last), None) == nv.EINVAL
+    assert lib.nvfp4_kv_window_pages(100, 64, 0, 0, 0, 10, 16, 8, None, ctypes.byref(last),
+                                     None) == nv.EINVAL
+    # a non-empty list needs the device array
+    assert lib.nvfp4_kv_window_pages(100, 64, 0, 0, 0, 10, None, 8, ctypes.byref(n),
+                                     ctypes.byref(last), None) == nv.EINVAL

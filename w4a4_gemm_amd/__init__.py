@@ -20,7 +20,7 @@ __all__ = [
     "NVFP4Tensor", "KVCache", "LIB_PATH",
     "nvfp4_abi_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_kv_page_bytes",
     "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm_w4a4",
-    "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks", "nvfp4_kv_attention",
+    "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks", "nvfp4_kv_attention", "nvfp4_kv_window_pages",
     "SCALES_ROWMAJOR", "SCALES_TILED", "OP_QUANTIZE", "OP_KV_QUANTIZE", "OP_KV_ATTENTION",
 ]
 
@@ -36,7 +36,7 @@ ABI_VERSION = 1
 EXPORTS = (
     "nvfp4_abi_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_kv_page_bytes",
     "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm_w4a4",
-    "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks", "nvfp4_kv_attention",
+    "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks", "nvfp4_kv_attention", "nvfp4_kv_window_pages",
 )
 
 
@@ -79,6 +79,8 @@ def _load():
                                                    vp]),
         "nvfp4_kv_attention": (ctypes.c_int, [ctypes.POINTER(_KVCache), i32, vp, i32, i32, vp, i64,
                                               ctypes.c_float, vp, vp, sz, vp]),
+        "nvfp4_kv_window_pages": (ctypes.c_int, [i64, i32, i64, i64, i64, i64, vp, i32,
+                                                 ctypes.POINTER(i32), ctypes.POINTER(i32), vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)            # AttributeError if the symbol is missing
@@ -281,3 +283,23 @@ def nvfp4_kv_attention(cache, layer, logical_pages, last_page_tokens, q, softmax
                                  _stream(stream))
     _check(st, "nvfp4_kv_attention")
     return out
+
+
+def nvfp4_kv_window_pages(total_tokens, page_tokens, global_sink_tokens, shot_start,
+                          shot_sink_tokens, window_tokens, pages=None, max_pages=None,
+                          device="cuda", stream=None):
+    """Logical page list of a multi-shot sink window -> (device int32 pages, last_page_tokens).
+
+    ``pages`` (device int32) receives the list; by default one is allocated with room for
+    every page of the cache.  The returned tensor is the filled prefix."""
+    if pages is None:
+        n_max = max(1, -(-total_tokens // page_tokens))
+        pages = torch.empty(n_max, dtype=torch.int32, device=device)
+    if max_pages is None:
+        max_pages = pages.numel()
+    n, last = ctypes.c_int32(0), ctypes.c_int32(0)
+    st = _lib.nvfp4_kv_window_pages(total_tokens, page_tokens, global_sink_tokens, shot_start,
+                                    shot_sink_tokens, window_tokens, _ptr(pages), max_pages,
+                                    ctypes.byref(n), ctypes.byref(last), _stream(stream))
+    _check(st, "nvfp4_kv_window_pages")
+    return pages[:n.value], last.value

@@ -3,6 +3,8 @@
 // synchronisation, no library state.
 
 #include "nvfp4.h"
+#include <climits>
+#include <cstdint>
 
 #include <hip/hip_runtime.h>
 
@@ -222,6 +224,71 @@ int nvfp4_kv_attention(const nvfp4_kv_cache_t* cache, int32_t layer,
   nvfp4::launch_kv_attention(g, logical_pages, n_pages, last_page_tokens, (const uint16_t*)q_bf16,
                              n_q, softmax_scale, (uint16_t*)out_bf16, workspace,
                              as_stream(stream));
+  return finish();
+}
+
+int nvfp4_kv_window_pages(int64_t total_tokens, int32_t page_tokens, int64_t global_sink_tokens,
+                          int64_t shot_start, int64_t shot_sink_tokens, int64_t window_tokens,
+                          int32_t* pages_dev, int32_t max_pages, int32_t* n_pages,
+                          int32_t* last_page_tokens, void* stream) {
+  if (!n_pages || !last_page_tokens) return NVFP4_EINVAL;
+  if (total_tokens < 0 || page_tokens <= 0 || global_sink_tokens < 0 || shot_start < 0 ||
+      shot_sink_tokens < 0 || window_tokens < 0 || max_pages < 0)
+    return NVFP4_EINVAL;
+  const int64_t P = page_tokens;
+  if ((total_tokens + P - 1) / P > INT32_MAX) return NVFP4_ESHAPE;
+  // the three token ranges, clipped, as page ranges [a, b)
+  int64_t ra[3], rb[3];
+  int n = 0;
+  const int64_t tok[3][2] = {{0, global_sink_tokens},
+                             {shot_start, shot_start + shot_sink_tokens},
+                             {total_tokens - window_tokens, total_tokens}};
+  for (int i = 0; i < 3; ++i) {
+    const int64_t a = tok[i][0] < 0 ? 0 : tok[i][0];
+    const int64_t b = tok[i][1] > total_tokens ? total_tokens : tok[i][1];
+    if (a < b) {
+      ra[n] = a / P;
+      rb[n] = (b + P - 1) / P;
+      ++n;
+    }
+  }
+  // sort by start (at most 3 ranges) and merge overlapping or touching ones
+  for (int i = 0; i < n; ++i)
+    for (int j = i + 1; j < n; ++j)
+      if (ra[j] < ra[i]) {
+        const int64_t ta = ra[i], tb = rb[i];
+        ra[i] = ra[j];
+        rb[i] = rb[j];
+        ra[j] = ta;
+        rb[j] = tb;
+      }
+  int m = 0;
+  for (int i = 0; i < n; ++i) {
+    if (m > 0 && ra[i] <= rb[m - 1]) {
+      if (rb[i] > rb[m - 1]) rb[m - 1] = rb[i];
+    } else {
+      ra[m] = ra[i];
+      rb[m] = rb[i];
+      ++m;
+    }
+  }
+  int64_t count = 0;
+  for (int i = 0; i < m; ++i) count += rb[i] - ra[i];
+  if (count > max_pages) return NVFP4_ESHAPE;
+  *n_pages = (int32_t)count;
+  *last_page_tokens =
+      count ? (int32_t)(total_tokens - P * (rb[m - 1] - 1) < P ? total_tokens - P * (rb[m - 1] - 1) : P)
+            : 0;
+  if (count == 0) return NVFP4_OK;
+  if (!pages_dev) return NVFP4_EINVAL;
+  if (!aligned(pages_dev, 4)) return NVFP4_ESHAPE;
+  int32_t r[6] = {0, 0, 0, 0, 0, 0};
+  for (int i = 0; i < m; ++i) {
+    r[2 * i] = (int32_t)ra[i];
+    r[2 * i + 1] = (int32_t)rb[i];
+  }
+  (void)hipGetLastError();
+  nvfp4::launch_kv_window_pages(r, m, (int32_t)count, pages_dev, as_stream(stream));
   return finish();
 }
 

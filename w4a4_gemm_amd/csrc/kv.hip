@@ -551,6 +551,24 @@ void launch_kv_quantize(const KvGeom& g, int32_t chunk_id, const uint16_t* k, co
                      chunk_id, ws, nsw, nfw, g, g.n_phys_pages, (const float*)mu);
 }
 
+// Entry i of the list: the i-th page of the concatenated ranges.
+__global__ __launch_bounds__(256) void kv_window_pages_kernel(int32_t a0, int32_t b0, int32_t a1,
+                                                              int32_t b1, int32_t a2,
+                                                              int32_t count,
+                                                              int32_t* __restrict__ pages) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  const int64_t l0 = b0 - a0, l1 = b1 - a1;
+  pages[i] = (int32_t)(i < l0 ? a0 + i : (i < l0 + l1 ? a1 + (i - l0) : a2 + (i - l0 - l1)));
+}
+
+void launch_kv_window_pages(const int32_t* r, int m, int32_t count, int32_t* pages,
+                            hipStream_t stream) {
+  (void)m;                                  // unused ranges are empty ([0, 0))
+  hipLaunchKernelGGL(kv_window_pages_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
+                     stream, r[0], r[1], r[2], r[3], r[4], count, pages);
+}
+
 #ifndef NVFP4_KV_READ_TOKENS
 #define NVFP4_KV_READ_TOKENS 8
 #endif

@@ -55,6 +55,11 @@ void launch_kv_attention(const KvGeom& g, const int32_t* logical_pages, int32_t 
                          float softmax_scale, uint16_t* out, void* workspace,
                          hipStream_t stream);
 
+// Page list of a window (kv.hip): `ranges` holds m disjoint, increasing page
+// ranges [r[2i], r[2i+1]) with `count` pages in total.
+void launch_kv_window_pages(const int32_t* ranges, int m, int32_t count, int32_t* pages,
+                            hipStream_t stream);
+
 void launch_kv_dequant(const KvGeom& g, const int32_t* logical_pages, int32_t n_pages,
                        uint16_t* k_out, uint16_t* v_out, hipStream_t stream);
 
