@@ -17,7 +17,12 @@ What it computes, and where the pages define it:
   4-bit" (techwalker summary, section 四, first key).
 * The NVFP4 KV cache: K mean-subtracted, then NVFP4-quantized; many cache
   blocks of a window dequantized at once (techwalker summary, section 四,
-  second key).
+  second key), attention over such a window, and the multi-shot sink window
+  as a page list (techwalker summary, section 六).
+* The producer-fused activation quantize: LayerNorm + adaLN modulate + NVFP4
+  in one step (zuobiaodaohang LongLive blog, section "NVFP4：数据体积砍到
+  1/4"; ai-manual.ru LongLive-2.0 article, section "Как это работает под
+  капотом").
 
 Every rounding is a single round-to-nearest-even of the exact real value,
 evaluated with exact comparisons (fp64 products that are provably exact,
@@ -29,4 +34,4 @@ something other than itself (library conversions, exhaustive tables,
 closed forms, ``Fraction`` brute force, values printed on the pages).
 """
 
-from . import formats, nvfp4, kvcache  # noqa: F401
+from . import formats, nvfp4, kvcache, window, adaln  # noqa: F401

@@ -175,3 +175,28 @@ class LongContextKV:
 def attn_queries(n_q, h=KV_HEADS, d=KV_HEAD_DIM, seed=50, std=1.0) -> np.ndarray:
     """Queries [n_q, h, d] as bf16 bits (normal, so q.k / sqrt(d) is O(1))."""
     return to_bf16_bits(normal_f32((n_q, h, d), std, seed))
+
+
+# ------------------------------------------------------------------ adaLN producer
+
+ADALN_ROWS_PER_GROUP = 880        # one latent frame of tokens per modulation pair
+
+
+def adaln_modulation(n_groups, cols, seed=70, std=0.25):
+    """(shift, scale) fp32 [n_groups, cols] ~ N(0, std): one pair per latent frame."""
+    rng = np.random.default_rng(seed)
+    shift = rng.standard_normal((n_groups, cols), dtype=np.float32) * np.float32(std)
+    scale = rng.standard_normal((n_groups, cols), dtype=np.float32) * np.float32(std)
+    return shift, scale
+
+
+def adaln_input(m=4096, k=3072, seed=72, dtype="bf16"):
+    """Residual stream entering a DiT block [m, k]: attn-proj distribution
+    (N(0,1), 8 channels x20), as bf16 bits or fp32, plus its modulation."""
+    x32 = normal_f32((m, k), 1.0, seed)
+    ch = np.random.default_rng(seed + 1).choice(k, size=min(8, k), replace=False)
+    x32[:, ch] *= np.float32(20.0)
+    groups = -(-m // ADALN_ROWS_PER_GROUP)
+    shift, scale = adaln_modulation(groups, k, seed=seed + 2)
+    x = to_bf16_bits(x32) if dtype == "bf16" else x32
+    return {"x": x, "shift": shift, "scale": scale, "rows_per_group": ADALN_ROWS_PER_GROUP}
