@@ -82,7 +82,8 @@ typedef struct {
 typedef enum {
   NVFP4_OP_QUANTIZE = 0,
   NVFP4_OP_KV_QUANTIZE = 1,
-  NVFP4_OP_KV_ATTENTION = 2
+  NVFP4_OP_KV_ATTENTION = 2,
+  NVFP4_OP_ADALN_QUANTIZE = 3
 } nvfp4_op_t;
 
 /* Workspace (device bytes) a call needs.
@@ -90,6 +91,7 @@ typedef enum {
  *   NVFP4_OP_KV_QUANTIZE:  a = T (tokens), b = n_heads, c = head_dim
  *   NVFP4_OP_KV_ATTENTION: a = n_q, b = n_heads, c = n_pages * page_tokens
  *                          (0 when the window is not split over workgroups)
+ *   NVFP4_OP_ADALN_QUANTIZE: a = rows, b = cols, c unused
  * Returns 0 for a bad op id.  The workspace must be 256-byte aligned. */
 size_t nvfp4_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c);
 
@@ -109,6 +111,37 @@ size_t nvfp4_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c);
 int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                    const float* amax, const nvfp4_tensor_t* out, void* workspace,
                    size_t ws_bytes, void* stream);
+
+/* Fused producer of a DiT block's W4A4 activations: LayerNorm of each row of
+ * the residual X (no affine parameters), adaLN modulation, then NVFP4 -- one
+ * kernel pair instead of a normalisation kernel, a modulation kernel and a
+ * quantize (zuobiaodaohang LongLive blog, section "NVFP4：数据体积砍到 1/4":
+ * adaLN fused into one kernel; ai-manual.ru LongLive-2.0 article, section
+ * "Как это работает под капотом": scaling fused with quantization).
+ *   mu_r   = mean of row r,  var_r = mean of (x - mu_r)^2 (biased),
+ *   rstd_r = 1 / sqrt(var_r + eps)  -- evaluated in fp64, stored as fp32;
+ *   x'     = RN32(RN32(n * RN32(1 + scale[g][c])) + shift[g][c]),
+ *   n      = RN32(RN32(x - mu_r) * rstd_r),  g = r / rows_per_group
+ * (fp32, one rounding per operation, no fused multiply-add), and x' is
+ * quantized as nvfp4_quantize does with amax = max|x'|.  X is read twice
+ * (statistics + amax, then encode); x' never goes to memory.
+ *   x               rows x cols, fp32 or bf16, row stride ld_x elements;
+ *                   16-byte aligned, ld_x * elem % 16 == 0
+ *   shift, scale    fp32 [ceil(rows / rows_per_group)][cols], 16-byte aligned
+ *                   (one modulation pair per group of rows, e.g. a latent frame)
+ *   rows_per_group  >= 1
+ *   eps             finite, > 0
+ *   row_stats       out: fp32 [rows][2] = (mu_r, rstd_r), 8-byte aligned
+ *   out             (host struct) as for nvfp4_quantize
+ *   workspace       nvfp4_workspace_bytes(NVFP4_OP_ADALN_QUANTIZE, rows, cols, 0)
+ * rows == 0 or cols == 0: only s_g (1.0) is written.
+ * Errors: EINVAL (nulls, dtype, rows_per_group, eps), ESHAPE (as
+ * nvfp4_quantize), EWORKSPACE. */
+int nvfp4_adaln_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                         int64_t ld_x, const float* shift, const float* scale,
+                         int64_t rows_per_group, float eps, float* row_stats,
+                         const nvfp4_tensor_t* out, void* workspace, size_t ws_bytes,
+                         void* stream);
 
 /* Dequantize: y = RN(q * s_b * s_g) in y_dtype (fp32, or bf16 with one
  * rounding of the exact product).  y: rows x cols, row stride ld_y elements,

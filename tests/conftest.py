@@ -11,7 +11,11 @@ if ROOT not in sys.path:
 
 # The HIP library is built in-tree; build it here only if nothing is built yet.
 if not os.path.exists(os.path.join(ROOT, "w4a4_gemm_amd", "libnvfp4.so")):
-    from w4a4_gemm_amd import build as _build
+    import importlib.util
+    _spec = importlib.util.spec_from_file_location(
+        "w4a4_gemm_amd_build", os.path.join(ROOT, "w4a4_gemm_amd", "build.py"))
+    _build = importlib.util.module_from_spec(_spec)
+    _spec.loader.exec_module(_build)
     _build.build()
 
 

@@ -168,3 +168,38 @@ def test_window_pages_host_side():
     # a non-empty list needs the device array
     assert lib.nvfp4_kv_window_pages(100, 64, 0, 0, 0, 10, None, 8, ctypes.byref(n),
                                      ctypes.byref(last), None) == nv.EINVAL
+
+
+def test_adaln_quantize_argument_errors():
+    import w4a4_gemm_amd as nv
+    lib = nv._lib
+    T = nv._Tensor
+    good = T(16, 16, 64, 128, 64, nv.SCALES_ROWMAJOR)
+    ws = nv.nvfp4_workspace_bytes(nv.OP_ADALN_QUANTIZE, 128, 64, 0)
+    assert ws > 0
+
+    def call(x=256, dtype=nv.BF16, rows=128, cols=64, ld=64, sh=512, sc=512, rpg=880, eps=1e-6,
+             stats=512, out=good, w=256, wb=ws):
+        return lib.nvfp4_adaln_quantize(x, dtype, rows, cols, ld, sh, sc, rpg, eps, stats,
+                                        ctypes.byref(out), w, wb, None)
+
+    assert call(dtype=9) == nv.EINVAL
+    assert call(rpg=0) == nv.EINVAL
+    assert call(eps=0.0) == nv.EINVAL
+    assert call(eps=-1.0) == nv.EINVAL
+    assert call(eps=float("inf")) == nv.EINVAL
+    assert call(eps=float("nan")) == nv.EINVAL
+    assert call(x=None) == nv.EINVAL
+    assert call(sh=None) == nv.EINVAL
+    assert call(sc=None) == nv.EINVAL
+    assert call(stats=None) == nv.EINVAL
+    assert call(rows=-1) == nv.EINVAL
+    assert call(cols=48, ld=48) == nv.ESHAPE                  # out->cols differs
+    assert call(ld=60) == nv.ESHAPE                           # ld * 2 % 16
+    assert call(sh=520) == nv.ESHAPE                          # shift not 16-byte aligned
+    assert call(stats=516) == nv.ESHAPE                       # stats not 8-byte aligned
+    assert call(w=None) == nv.EWORKSPACE
+    assert call(wb=ws - 4) == nv.EWORKSPACE
+    assert call(w=272) == nv.EWORKSPACE                       # not 256-byte aligned
+    tiled_bad = T(16, 16, 64, 100, 64, nv.SCALES_TILED)
+    assert call(rows=100, out=tiled_bad) == nv.ESHAPE

@@ -19,9 +19,10 @@ import torch
 __all__ = [
     "NVFP4Tensor", "KVCache", "LIB_PATH",
     "nvfp4_abi_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_kv_page_bytes",
-    "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm_w4a4",
+    "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm_w4a4", "nvfp4_adaln_quantize",
     "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks", "nvfp4_kv_attention", "nvfp4_kv_window_pages",
     "SCALES_ROWMAJOR", "SCALES_TILED", "OP_QUANTIZE", "OP_KV_QUANTIZE", "OP_KV_ATTENTION",
+    "OP_ADALN_QUANTIZE",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so")
@@ -30,12 +31,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so
 OK, EINVAL, ESHAPE, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 SCALES_ROWMAJOR, SCALES_TILED = 0, 1
-OP_QUANTIZE, OP_KV_QUANTIZE, OP_KV_ATTENTION = 0, 1, 2
+OP_QUANTIZE, OP_KV_QUANTIZE, OP_KV_ATTENTION, OP_ADALN_QUANTIZE = 0, 1, 2, 3
 ABI_VERSION = 1
 
 EXPORTS = (
     "nvfp4_abi_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_kv_page_bytes",
-    "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm_w4a4",
+    "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm_w4a4", "nvfp4_adaln_quantize",
     "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks", "nvfp4_kv_attention", "nvfp4_kv_window_pages",
 )
 
@@ -59,7 +60,7 @@ class _KVCache(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m w4a4_gemm_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python w4a4_gemm_amd/build.py` "
             "(there is no fallback path)")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -71,6 +72,8 @@ def _load():
         "nvfp4_quantize": (ctypes.c_int, [vp, i32, i64, i64, i64, vp, ctypes.POINTER(_Tensor),
                                           vp, sz, vp]),
         "nvfp4_dequantize": (ctypes.c_int, [ctypes.POINTER(_Tensor), vp, i32, i64, vp]),
+        "nvfp4_adaln_quantize": (ctypes.c_int, [vp, i32, i64, i64, i64, vp, vp, i64, ctypes.c_float,
+                                                vp, ctypes.POINTER(_Tensor), vp, sz, vp]),
         "nvfp4_gemm_w4a4": (ctypes.c_int, [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), vp,
                                            i32, i64, vp, vp]),
         "nvfp4_kv_quantize": (ctypes.c_int, [ctypes.POINTER(_KVCache), i32, i32, vp, vp, i64, i64,
@@ -83,7 +86,10 @@ def _load():
                                                  ctypes.POINTER(i32), ctypes.POINTER(i32), vp]),
     }
     for name, (res, args) in sig.items():
-        fn = getattr(lib, name)            # AttributeError if the symbol is missing
+        if not hasattr(lib, name):
+            raise ImportError(f"{LIB_PATH} lacks {name}: rebuild it with "
+                              "`python w4a4_gemm_amd/build.py`")
+        fn = getattr(lib, name)
         fn.restype, fn.argtypes = res, args
     if lib.nvfp4_abi_version() != ABI_VERSION:
         raise ImportError("libnvfp4.so ABI version mismatch: rebuild the library")
@@ -174,6 +180,37 @@ def nvfp4_quantize(x, layout=SCALES_TILED, amax=None, out=None, workspace=None, 
                              workspace.numel() if workspace is not None else 0, _stream(stream))
     _check(st, "nvfp4_quantize")
     return out
+
+
+def nvfp4_adaln_quantize(x, shift, scale, rows_per_group, eps=1e-6, layout=SCALES_TILED,
+                         out=None, row_stats=None, workspace=None, stream=None):
+    """LayerNorm + adaLN modulate + NVFP4 of a 2-D bf16/fp32 CUDA tensor -> (NVFP4Tensor, row_stats).
+
+    ``shift``/``scale``: fp32 [ceil(rows / rows_per_group), cols]; ``row_stats``
+    receives fp32 [rows, 2] = (mean, rstd) per row."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    for v in (shift, scale):
+        if v.dtype != torch.float32 or not v.is_contiguous():
+            raise ValueError("shift and scale must be contiguous fp32")
+    rows, cols = x.shape
+    groups = -(-rows // rows_per_group) if rows_per_group > 0 else 0
+    if rows and cols and (shift.shape != (groups, cols) or scale.shape != (groups, cols)):
+        raise ValueError(f"shift/scale must be [{groups}, {cols}]")
+    if out is None:
+        out = NVFP4Tensor(rows, cols, layout, device=x.device)
+    if row_stats is None:
+        row_stats = torch.empty((rows, 2), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(nvfp4_workspace_bytes(OP_ADALN_QUANTIZE, rows, cols, 0),
+                                dtype=torch.uint8, device=x.device)
+    cs = out.c()
+    st = _lib.nvfp4_adaln_quantize(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0),
+                                   _ptr(shift), _ptr(scale), rows_per_group, eps, _ptr(row_stats),
+                                   ctypes.byref(cs), _ptr(workspace), workspace.numel(),
+                                   _stream(stream))
+    _check(st, "nvfp4_adaln_quantize")
+    return out, row_stats
 
 
 def nvfp4_dequantize(t, dtype=torch.float32, out=None, stream=None):

@@ -10,7 +10,10 @@ Flags:
 * ``-fno-gpu-flush-denormals-to-zero`` -- fp32 subnormals are kept, which the
   exact rounding in the kernels relies on.
 
-Usage:  python -m w4a4_gemm_amd.build  [-v]
+Usage:  python w4a4_gemm_amd/build.py  [-v]
+
+Run it as a script (or load it by path): importing the package loads the
+library and checks its symbols, which fails while the library is stale.
 """
 
 import os

@@ -4,6 +4,7 @@
 
 #include "nvfp4.h"
 #include <climits>
+#include <cmath>
 #include <cstdint>
 
 #include <hip/hip_runtime.h>
@@ -64,6 +65,7 @@ size_t nvfp4_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c) {
   switch (op) {
     case NVFP4_OP_QUANTIZE: return nvfp4::quantize_workspace_bytes(a, b, c != 0);
     case NVFP4_OP_KV_QUANTIZE: return nvfp4::kv_quantize_workspace_bytes(a, b, c);
+    case NVFP4_OP_ADALN_QUANTIZE: return nvfp4::adaln_quantize_workspace_bytes(a, b);
     case NVFP4_OP_KV_ATTENTION:
       return a < 0 || b <= 0 || c < 0 ? 0 : nvfp4::kv_attention_workspace_bytes(a, b, c);
     default: return 0;
@@ -89,6 +91,32 @@ int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, i
   nvfp4::launch_quantize(x, x_dtype == NVFP4_BF16, rows, cols, ld_x, amax, out->codes,
                          out->scales, out->scale_layout == NVFP4_SCALES_TILED,
                          out->global_scale, workspace, as_stream(stream));
+  return finish();
+}
+
+int nvfp4_adaln_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                         int64_t ld_x, const float* shift, const float* scale,
+                         int64_t rows_per_group, float eps, float* row_stats,
+                         const nvfp4_tensor_t* out, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (rows < 0 || cols < 0 || rows_per_group < 1) return NVFP4_EINVAL;
+  if (!(eps > 0.0f) || !(eps < INFINITY)) return NVFP4_EINVAL;
+  int st = check_tensor(out);
+  if (st) return st;
+  if (out->rows != rows || out->cols != cols) return NVFP4_ESHAPE;
+  const int64_t elem = x_dtype == NVFP4_BF16 ? 2 : 4;
+  if (ld_x < cols || (ld_x * elem) % 16) return NVFP4_ESHAPE;
+  if (rows > 0 && cols > 0 && (!x || !shift || !scale || !row_stats)) return NVFP4_EINVAL;
+  if (!aligned(x, 16) || !aligned(shift, 16) || !aligned(scale, 16) || !aligned(row_stats, 8))
+    return NVFP4_ESHAPE;
+  const size_t need = nvfp4::adaln_quantize_workspace_bytes(rows, cols);
+  if (!workspace || ws_bytes < need || !aligned(workspace, 256)) return NVFP4_EWORKSPACE;
+  (void)hipGetLastError();
+  nvfp4::launch_adaln_quantize(x, x_dtype == NVFP4_BF16, rows, cols, ld_x, shift, scale,
+                               rows_per_group, eps, row_stats, out->codes, out->scales,
+                               out->scale_layout == NVFP4_SCALES_TILED, out->global_scale,
+                               workspace, as_stream(stream));
   return finish();
 }
 

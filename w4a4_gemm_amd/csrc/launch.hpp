@@ -23,6 +23,15 @@ void launch_dequantize(const uint8_t* codes, const uint8_t* scales, bool tiled,
                        const float* gscale, int64_t rows, int64_t cols, void* y, bool y_bf16,
                        int64_t ld_y, hipStream_t stream);
 
+// Fused LayerNorm + adaLN modulate + quantize (quant.hip); row_stats is
+// [rows][2] fp32 (mean, rstd), shift/scale [groups][cols] fp32.
+size_t adaln_quantize_workspace_bytes(int64_t rows, int64_t cols);
+
+void launch_adaln_quantize(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ld,
+                           const float* shift, const float* scale, int64_t rows_per_group,
+                           float eps, float* row_stats, uint8_t* codes, uint8_t* scales,
+                           bool tiled, float* gscale, void* workspace, hipStream_t stream);
+
 // ---- W4A4 GEMM (gemm.hip)
 void launch_gemm(const uint8_t* xc, const uint8_t* xs, bool x_tiled, const float* xg,
                  const uint8_t* wc, const uint8_t* ws, bool w_tiled, const float* wg,

@@ -152,16 +152,19 @@ __global__ __launch_bounds__(64) void publish_gscale_kernel(const float* __restr
 
 // The 8 row tasks of a lane.  kPre: s_g < 2^-100, x is scaled by 2^64 before
 // encoding (a tensor-uniform choice, so the two variants are separate code).
-template <bool kBf16, bool kTiled, bool kPre>
+// `pro(t, v)` maps task t's 8 loaded values to the values that are quantized
+// (the identity for a plain quantize).
+template <bool kBf16, bool kTiled, bool kPre, typename Prologue>
 __device__ __forceinline__ void quantize_tasks(const Raw8* raw, const TensorEnc& te, int64_t r0,
                                                int64_t rows, bool cok, int j,
                                                uint8_t* __restrict__ cp,
                                                uint8_t* __restrict__ sp, int64_t c_step,
-                                               int64_t s_step) {
+                                               int64_t s_step, const Prologue& pro) {
 #pragma unroll
   for (int t = 0; t < kTasks; ++t) {
     float v[8];
     unpack8<kBf16>(raw[t], v);
+    pro(t, v);
     float bm = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) bm = fmaxf(bm, __builtin_fabsf(v[e]));
@@ -217,10 +220,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(
                                  : r0 * (cols / 16) + kb);
   const int64_t c_step = 4 * (cols / 2);
   const int64_t s_step = kTiled ? 16 : 4 * (cols / 16);   // tiled: 128-row tiles hold all 8 tasks
+  const auto identity = [](int, float*) {};
   if (te.pre != 1.0f)
-    quantize_tasks<kBf16, kTiled, true>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step);
+    quantize_tasks<kBf16, kTiled, true>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
+                                        identity);
   else
-    quantize_tasks<kBf16, kTiled, false>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step);
+    quantize_tasks<kBf16, kTiled, false>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
+                                         identity);
 }
 
 // ------------------------------------------------------------------ dequantize
@@ -288,6 +294,235 @@ __global__ __launch_bounds__(256) void dequantize_kernel(
   }
 }
 
+// ------------------------------------------------------------------ fused LayerNorm + adaLN + quantize
+//
+// The producer of a W4A4 linear's activations in a DiT block: LayerNorm of
+// each residual row (no affine parameters), the adaLN modulation
+// x' = n (1 + scale) + shift with one (shift, scale) pair per group of rows,
+// then NVFP4 -- adaLN fused into one kernel (zuobiaodaohang LongLive blog,
+// section "NVFP4：数据体积砍到 1/4") and scaling fused with quantization
+// (ai-manual.ru LongLive-2.0 article, section "Как это работает под
+// капотом").  Two passes over x, as for a plain quantize: the stats pass
+// writes each row's (mean, rstd) and per-workgroup maxima of |x'|; the encode
+// pass recomputes x' from x and the stored statistics and encodes it.  x'
+// itself never goes to memory.
+
+// x' of one element: fp32, one rounding per operation in the formula's order
+// (no contraction into fused multiply-adds), so both passes get the same bits.
+__device__ __forceinline__ float adaln_value(float x, float mu, float rstd, float gain,
+                                             float shift) {
+#pragma clang fp contract(off)
+  const float n = (x - mu) * rstd;
+  return n * gain + shift;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <bool kBf16>
+__device__ __forceinline__ void chunk_values(const u32x4 w, float* v) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (kBf16) {
+      v[2 * j] = bf16_lo(w[j]);
+      v[2 * j + 1] = bf16_hi(w[j]);
+    } else {
+      v[j] = __uint_as_float(w[j]);
+    }
+  }
+}
+
+__device__ __forceinline__ void load_f32(const float* __restrict__ p, float* v, int n) {
+#pragma unroll
+  for (int k = 0; k < n / 4; ++k) {
+    const f32x4 w = *(const f32x4*)(p + 4 * k);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[4 * k + e] = w[e];
+  }
+}
+
+constexpr int kStatRegChunks = 8;   // 16-byte chunks of a row a lane keeps in registers
+
+// One wave, one row: statistics (fp64 sums; mean and rstd rounded once to
+// fp32), stored by lane 0; returns this lane's max |x'|.  kRegs: the row
+// (at most 64 kStatRegChunks chunks) stays in registers across the three
+// sweeps; otherwise each sweep reads it again (from cache).
+template <bool kBf16, bool kRegs>
+__device__ __forceinline__ float adaln_row(const u32x4* __restrict__ xr, int64_t cpr,
+                                           int64_t cols, const float* __restrict__ sh,
+                                           const float* __restrict__ sc, float eps, int lane,
+                                           float2* __restrict__ st) {
+  constexpr int kPer = kBf16 ? 8 : 4;
+  constexpr int kU = kRegs ? kStatRegChunks : 1;
+  u32x4 w[kU];
+  if (kRegs) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t i = lane + 64 * u;
+      w[u] = i < cpr ? xr[i] : u32x4{0, 0, 0, 0};
+    }
+  }
+  auto for_chunks = [&](auto&& f) {
+    if (kRegs) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t i = lane + 64 * u;
+        if (i < cpr) {
+          float v[kPer];
+          chunk_values<kBf16>(w[u], v);
+          f(i, v);
+        }
+      }
+    } else {
+      for (int64_t i = lane; i < cpr; i += 64) {
+        float v[kPer];
+        chunk_values<kBf16>(xr[i], v);
+        f(i, v);
+      }
+    }
+  };
+  double s = 0.0;
+  for_chunks([&](int64_t, const float* v) {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) s += (double)v[e];
+  });
+  const double mean = wave_sum(s) / (double)cols;
+  double q = 0.0;
+  for_chunks([&](int64_t, const float* v) {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const double d = (double)v[e] - mean;
+      q += d * d;
+    }
+  });
+  const double var = wave_sum(q) / (double)cols;
+  const float mu = (float)mean;
+  const float rstd = (float)(1.0 / sqrt(var + (double)eps));
+  float m = 0.0f;
+  for_chunks([&](int64_t i, const float* v) {
+    float shv[kPer], scv[kPer];
+    load_f32(sh + i * kPer, shv, kPer);
+    load_f32(sc + i * kPer, scv, kPer);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      m = fmaxf(m, __builtin_fabsf(adaln_value(v[e], mu, rstd, 1.0f + scv[e], shv[e])));
+  });
+  if (lane == 0) *st = make_float2(mu, rstd);
+  return m;
+}
+
+// Stats pass: wave w of workgroup b takes rows 4 b + w, 4 b + w + 4 G, ...
+// (G workgroups); every workgroup writes its partial max |x'| (0 if idle).
+template <bool kBf16>
+__global__ __launch_bounds__(256) void adaln_stats_kernel(
+    const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+    const float* __restrict__ shift, const float* __restrict__ scale, int64_t rpg, float eps,
+    float2* __restrict__ stats, float* __restrict__ partial) {
+  const int lane = threadIdx.x & 63;
+  const int64_t cpr = cols / (kBf16 ? 8 : 4);
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  float m = 0.0f;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows; r += nw) {
+    const u32x4* xr = (const u32x4*)((const char*)x + r * ld * (kBf16 ? 2 : 4));
+    const int64_t g = r / rpg;
+    if (cpr <= 64 * kStatRegChunks)
+      m = fmaxf(m, adaln_row<kBf16, true>(xr, cpr, cols, shift + g * cols, scale + g * cols, eps,
+                                          lane, stats + r));
+    else
+      m = fmaxf(m, adaln_row<kBf16, false>(xr, cpr, cols, shift + g * cols, scale + g * cols,
+                                           eps, lane, stats + r));
+  }
+  m = wave_max(m);
+  __shared__ float red[4];
+  if (lane == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// Encode pass: the plain quantize tiling, with x' computed from the loaded x in
+// the prologue.  kTwoGroups: rows_per_group > 4 (kTasks - 1), so a lane's rows
+// r0 .. r0 + 4 (kTasks - 1) meet at most two modulation groups, whose vectors
+// are loaded once; otherwise each task loads its own.
+template <bool kBf16, bool kTiled, bool kTwoGroups>
+__global__ __launch_bounds__(256) void adaln_quantize_kernel(
+    const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+    const float* __restrict__ shift, const float* __restrict__ scale, int64_t rpg,
+    const float2* __restrict__ stats, const float* __restrict__ partial,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gscale) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int64_t c0 = (int64_t)blockIdx.y * kTile + 8 * j;
+  const int64_t r0 = (int64_t)blockIdx.x * kTile + 32 * wave + (lane >> 4);
+  const bool cok = c0 < cols;
+
+  const Partials part = load_partials(partial);
+  const int64_t cl = cok ? c0 : cols - 8;
+  Raw8 raw[kTasks];
+  float2 st[kTasks];
+#pragma unroll
+  for (int t = 0; t < kTasks; ++t) {
+    const int64_t r = r0 + 4 * t;
+    const int64_t rc = r < rows ? r : rows - 1;
+    raw[t] = load8<kBf16>(x, rc * ld + cl);
+    st[t] = stats[rc];
+  }
+  const int64_t ra = r0 < rows ? r0 : rows - 1;
+  const int64_t ga = ra / rpg;
+  const int64_t next = (ga + 1) * rpg;      // first row of the following group
+  float sha[8], gna[8], shb[8], gnb[8];
+  if (kTwoGroups) {
+    const int64_t gb = ga + 1 < (rows + rpg - 1) / rpg ? ga + 1 : ga;
+    load_f32(shift + ga * cols + cl, sha, 8);
+    load_f32(scale + ga * cols + cl, gna, 8);
+    load_f32(shift + gb * cols + cl, shb, 8);
+    load_f32(scale + gb * cols + cl, gnb, 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      gna[e] = 1.0f + gna[e];
+      gnb[e] = 1.0f + gnb[e];
+    }
+  }
+  const auto modulate = [&](int t, float* v) {
+    const int64_t r = r0 + 4 * t;
+    const int64_t rc = r < rows ? r : rows - 1;
+    if (kTwoGroups) {
+      const bool b = rc >= next;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        v[e] = adaln_value(v[e], st[t].x, st[t].y, b ? gnb[e] : gna[e], b ? shb[e] : sha[e]);
+    } else {
+      const int64_t g = rc / rpg;
+      float sh[8], gn[8];
+      load_f32(shift + g * cols + cl, sh, 8);
+      load_f32(scale + g * cols + cl, gn, 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = adaln_value(v[e], st[t].x, st[t].y, 1.0f + gn[e], sh[e]);
+    }
+  };
+
+  float s_g = global_scale(reduce_partials(part));
+  s_g = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_g)));   // uniform
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *gscale = s_g;
+  const TensorEnc te = make_tensor_enc(s_g);
+
+  const int64_t kb = c0 >> 4;
+  uint8_t* cp = codes + r0 * (cols / 2) + c0 / 2;
+  uint8_t* sp = scales + (kTiled ? ((r0 >> 7) * (cols / 64) + (kb >> 2)) * 512 +
+                                       (r0 & 127) * 4 + (kb & 3)
+                                 : r0 * (cols / 16) + kb);
+  const int64_t c_step = 4 * (cols / 2);
+  const int64_t s_step = kTiled ? 16 : 4 * (cols / 16);
+  if (te.pre != 1.0f)
+    quantize_tasks<kBf16, kTiled, true>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
+                                        modulate);
+  else
+    quantize_tasks<kBf16, kTiled, false>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
+                                         modulate);
+}
+
 // ------------------------------------------------------------------ launchers
 
 size_t quantize_workspace_bytes(int64_t rows, int64_t cols, bool has_amax) {
@@ -343,6 +578,50 @@ void launch_dequantize(const uint8_t* codes, const uint8_t* scales, bool tiled,
     else NVFP4_DLAUNCH(false, false);
   }
 #undef NVFP4_DLAUNCH
+}
+
+size_t adaln_quantize_workspace_bytes(int64_t rows, int64_t cols) {
+  (void)rows;
+  (void)cols;
+  return (size_t)kAmaxPartials * sizeof(float);
+}
+
+void launch_adaln_quantize(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ld,
+                           const float* shift, const float* scale, int64_t rows_per_group,
+                           float eps, float* row_stats, uint8_t* codes, uint8_t* scales,
+                           bool tiled, float* gscale, void* workspace, hipStream_t stream) {
+  float* partial = (float*)workspace;
+  float2* stats = (float2*)row_stats;
+  // cols == 0: no row has statistics; only s_g (1) is published
+  const int64_t srows = cols > 0 ? rows : 0;
+  if (x_bf16)
+    hipLaunchKernelGGL(adaln_stats_kernel<true>, dim3(kAmaxPartials), dim3(256), 0, stream, x,
+                       srows, cols, ld, shift, scale, rows_per_group, eps, stats, partial);
+  else
+    hipLaunchKernelGGL(adaln_stats_kernel<false>, dim3(kAmaxPartials), dim3(256), 0, stream, x,
+                       srows, cols, ld, shift, scale, rows_per_group, eps, stats, partial);
+  if (rows == 0 || cols == 0) {
+    hipLaunchKernelGGL(publish_gscale_kernel, dim3(1), dim3(64), 0, stream, nullptr, partial,
+                       gscale);
+    return;
+  }
+  const dim3 grid((unsigned)((rows + kTile - 1) / kTile), (unsigned)((cols + kTile - 1) / kTile));
+  const bool two = rows_per_group > 4 * (kTasks - 1);
+  const auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, x, rows, cols, ld, shift, scale,
+                       rows_per_group, stats, partial, codes, scales, gscale);
+  };
+  if (x_bf16) {
+    if (tiled) two ? go(adaln_quantize_kernel<true, true, true>)
+                   : go(adaln_quantize_kernel<true, true, false>);
+    else two ? go(adaln_quantize_kernel<true, false, true>)
+             : go(adaln_quantize_kernel<true, false, false>);
+  } else {
+    if (tiled) two ? go(adaln_quantize_kernel<false, true, true>)
+                   : go(adaln_quantize_kernel<false, true, false>);
+    else two ? go(adaln_quantize_kernel<false, false, true>)
+             : go(adaln_quantize_kernel<false, false, false>);
+  }
 }
 
 }  // namespace nvfp4
