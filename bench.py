@@ -84,8 +84,15 @@ def op_table():
 def next_op_table():
     """Algorithmic work of the rows measured beside the step."""
     keys = 68 * 256
+    m, k, groups = 8192, 3072, -(-8192 // 880)
     return {"kv_attention": {"flops": 4 * ATTN_QUERIES * keys * 128 * 24,
-                             "compressed_bytes": 68 * 2 * 24 * 256 * (64 + 8)}}
+                             "compressed_bytes": 68 * 2 * 24 * 256 * (64 + 8),
+                             "workload": (f"{ATTN_QUERIES} queries x 24 heads x 128 over a 68-page "
+                                          "window (17408 keys), pages read as NVFP4; bf16 MFMA")},
+            # x read once, NVFP4 written, row stats written, modulation read once
+            "adaln_quantize": {"bytes": m * k * (2 + NV_ELEM) + 4 + 8 * m + 2 * groups * k * 4,
+                               "workload": ("FFN input 8192x3072 bf16: LayerNorm + adaLN modulate "
+                                            "(880-row groups) + NVFP4, tiled scales")}}
 
 
 def roofline_seconds(op):
@@ -153,6 +160,16 @@ class Workload:
         self.attn_q = bf16(synth.attn_queries(ATTN_QUERIES, r.H, r.D, seed=50))
         self.attn_out = torch.empty_like(self.attn_q)
         self.attn_last = r.P
+        # next row: the FFN input produced by LayerNorm + adaLN + NVFP4 in one kernel pair
+        d = synth.adaln_input(m=8192, k=3072, seed=72)
+        self.ln_x = bf16(d["x"])
+        self.ln_shift = torch.from_numpy(d["shift"]).to(dev)
+        self.ln_scale = torch.from_numpy(d["scale"]).to(dev)
+        self.ln_rpg = d["rows_per_group"]
+        self.ln_q = nv.NVFP4Tensor(8192, 3072, nv.SCALES_TILED, device=dev)
+        self.ln_stats = torch.empty((8192, 2), dtype=torch.float32, device=dev)
+        self.ln_ws = torch.empty(nv.nvfp4_workspace_bytes(nv.OP_ADALN_QUANTIZE, 8192, 3072, 0),
+                                 dtype=torch.uint8, device=dev)
         self._ops = self.ops()
         torch.cuda.synchronize()
 
@@ -188,8 +205,11 @@ class Workload:
         """Rows built beyond the step, measured on their own."""
         nv = self.nv
         return [("kv_attention", lambda: nv.nvfp4_kv_attention(
-            self.lc, 0, self.window, self.attn_last, self.attn_q, 1.0 / 128 ** 0.5,
-            out=self.attn_out))]
+                    self.lc, 0, self.window, self.attn_last, self.attn_q, 1.0 / 128 ** 0.5,
+                    out=self.attn_out)),
+                ("adaln_quantize", lambda: nv.nvfp4_adaln_quantize(
+                    self.ln_x, self.ln_shift, self.ln_scale, self.ln_rpg, 1e-6, out=self.ln_q,
+                    row_stats=self.ln_stats, workspace=self.ln_ws))]
 
     def step(self, ev=None):
         """One pass of the hot path.  ``ev(name)`` records a timing event boundary."""
@@ -400,11 +420,13 @@ def main():
     nxt_rec = {}
     for n, o in next_op_table().items():
         t = nxt[n]
-        nxt_rec[n] = {"ms": round(t * 1e3, 4), "tflops": round(o["flops"] / t / 1e12, 2),
-                      "roofline_frac": round(o["flops"] / t / MFMA_F16_FLOPS, 4),
-                      "workload": (f"{ATTN_QUERIES} queries x 24 heads x 128 over a 68-page "
-                                   "window (17408 keys), pages read as NVFP4; bf16 MFMA"),
-                      "in_step": False}
+        rec = {"ms": round(t * 1e3, 4), "roofline_frac": round(roofline_seconds(o) / t, 4),
+               "workload": o["workload"], "in_step": False}
+        if "flops" in o:
+            rec["tflops"] = round(o["flops"] / t / 1e12, 2)
+        else:
+            rec["gbps"] = round(o["bytes"] / t / 1e9, 1)
+        nxt_rec[n] = rec
 
     g1 = per_op["ffn_gemm1"]
     line = {
