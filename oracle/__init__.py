@@ -23,6 +23,9 @@ What it computes, and where the pages define it:
   in one step (zuobiaodaohang LongLive blog, section "NVFP4：数据体积砍到
   1/4"; ai-manual.ru LongLive-2.0 article, section "Как это работает под
   капотом").
+* The training-side GEMMs (dgrad, wgrad) with operands quantized along the
+  contraction axis, including the transposed quantizer (techwalker summary,
+  sections 一 and 五: NVFP4 training and distillation).
 
 Every rounding is a single round-to-nearest-even of the exact real value,
 evaluated with exact comparisons (fp64 products that are provably exact,
@@ -34,4 +37,4 @@ something other than itself (library conversions, exhaustive tables,
 closed forms, ``Fraction`` brute force, values printed on the pages).
 """
 
-from . import formats, nvfp4, kvcache, window, adaln  # noqa: F401
+from . import formats, nvfp4, kvcache, window, adaln, training  # noqa: F401
