@@ -112,6 +112,29 @@ int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, i
                    const float* amax, const nvfp4_tensor_t* out, void* workspace,
                    size_t ws_bytes, void* stream);
 
+/* Transposed quantize: out = NVFP4 of X^T, i.e. output row k holds column k of
+ * X [rows x cols] and the blocks of 16 run along X's rows.  This is the operand
+ * layout of NVFP4 training's backward GEMMs (techwalker summary, sections 一
+ * and 五: NVFP4 training and distillation), which contract over the other axis
+ * of a forward operand; with it both run on nvfp4_gemm_w4a4 (Y = A B^T):
+ *   dgrad  dX = dY W     A = nvfp4_quantize(dY),  B = nvfp4_quantize_transposed(W)
+ *   wgrad  dW = dY^T X   A = nvfp4_quantize_transposed(dY),
+ *                        B = nvfp4_quantize_transposed(X)
+ * Same quantizer as nvfp4_quantize (round to nearest even, one s_g from the
+ * tensor amax, which a transposition leaves unchanged).
+ *   x          rows x cols, fp32 or bf16, row stride ld_x elements;
+ *              16-byte aligned, ld_x * elem % 16 == 0
+ *   amax       NULL, or a device float holding max|x| (X is then read once)
+ *   out        (host struct) out->rows == cols, out->cols == rows
+ *              (so rows % 16 == 0; tiled scales need cols % 128 and rows % 64)
+ *   workspace  nvfp4_workspace_bytes(NVFP4_OP_QUANTIZE, rows, cols, amax != NULL)
+ * rows == 0 or cols == 0: only s_g (1.0, or from amax) is written.
+ * Errors: EINVAL (nulls, dtype), ESHAPE (cols % 16, out dims, alignment,
+ * ld_x < cols), EWORKSPACE. */
+int nvfp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                              int64_t ld_x, const float* amax, const nvfp4_tensor_t* out,
+                              void* workspace, size_t ws_bytes, void* stream);
+
 /* Fused producer of a DiT block's W4A4 activations: LayerNorm of each row of
  * the residual X (no affine parameters), adaLN modulation, then NVFP4 -- one
  * kernel pair instead of a normalisation kernel, a modulation kernel and a

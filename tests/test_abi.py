@@ -203,3 +203,26 @@ def test_adaln_quantize_argument_errors():
     assert call(w=272) == nv.EWORKSPACE                       # not 256-byte aligned
     tiled_bad = T(16, 16, 64, 100, 64, nv.SCALES_TILED)
     assert call(rows=100, out=tiled_bad) == nv.ESHAPE
+
+
+def test_quantize_transposed_argument_errors():
+    import w4a4_gemm_amd as nv
+    lib = nv._lib
+    T = nv._Tensor
+    out = T(16, 16, 64, 64, 128, nv.SCALES_ROWMAJOR)        # X^T of a 128 x 64 input
+    ws = nv.nvfp4_workspace_bytes(nv.OP_QUANTIZE, 128, 64, 0)
+
+    def call(x=256, dtype=nv.BF16, rows=128, cols=64, ld=64, amax=None, o=out, w=256, wb=ws):
+        return lib.nvfp4_quantize_transposed(x, dtype, rows, cols, ld, amax, ctypes.byref(o), w,
+                                             wb, None)
+
+    assert call(dtype=5) == nv.EINVAL
+    assert call(x=None) == nv.EINVAL
+    assert call(rows=-16) == nv.EINVAL
+    assert call(rows=64) == nv.ESHAPE                         # out is not [cols x rows]
+    assert call(o=T(16, 16, 64, 128, 64, nv.SCALES_ROWMAJOR)) == nv.ESHAPE
+    assert call(cols=56, ld=56, o=T(16, 16, 64, 56, 128, nv.SCALES_ROWMAJOR)) == nv.ESHAPE
+    assert call(ld=60) == nv.ESHAPE
+    assert call(amax=258) == nv.ESHAPE
+    assert call(w=None) == nv.EWORKSPACE
+    assert call(o=T(16, 16, 64, 64, 128, nv.SCALES_TILED)) == nv.ESHAPE   # tiled needs 128 | out rows

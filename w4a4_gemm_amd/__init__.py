@@ -20,6 +20,7 @@ __all__ = [
     "NVFP4Tensor", "KVCache", "LIB_PATH",
     "nvfp4_abi_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_kv_page_bytes",
     "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm_w4a4", "nvfp4_adaln_quantize",
+    "nvfp4_quantize_transposed",
     "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks", "nvfp4_kv_attention", "nvfp4_kv_window_pages",
     "SCALES_ROWMAJOR", "SCALES_TILED", "OP_QUANTIZE", "OP_KV_QUANTIZE", "OP_KV_ATTENTION",
     "OP_ADALN_QUANTIZE",
@@ -37,6 +38,7 @@ ABI_VERSION = 1
 EXPORTS = (
     "nvfp4_abi_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_kv_page_bytes",
     "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm_w4a4", "nvfp4_adaln_quantize",
+    "nvfp4_quantize_transposed",
     "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks", "nvfp4_kv_attention", "nvfp4_kv_window_pages",
 )
 
@@ -72,6 +74,8 @@ def _load():
         "nvfp4_quantize": (ctypes.c_int, [vp, i32, i64, i64, i64, vp, ctypes.POINTER(_Tensor),
                                           vp, sz, vp]),
         "nvfp4_dequantize": (ctypes.c_int, [ctypes.POINTER(_Tensor), vp, i32, i64, vp]),
+        "nvfp4_quantize_transposed": (ctypes.c_int, [vp, i32, i64, i64, i64, vp,
+                                                     ctypes.POINTER(_Tensor), vp, sz, vp]),
         "nvfp4_adaln_quantize": (ctypes.c_int, [vp, i32, i64, i64, i64, vp, vp, i64, ctypes.c_float,
                                                 vp, ctypes.POINTER(_Tensor), vp, sz, vp]),
         "nvfp4_gemm_w4a4": (ctypes.c_int, [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), vp,
@@ -179,6 +183,26 @@ def nvfp4_quantize(x, layout=SCALES_TILED, amax=None, out=None, workspace=None, 
                              _ptr(amax), ctypes.byref(cs), _ptr(workspace),
                              workspace.numel() if workspace is not None else 0, _stream(stream))
     _check(st, "nvfp4_quantize")
+    return out
+
+
+def nvfp4_quantize_transposed(x, layout=SCALES_TILED, amax=None, out=None, workspace=None,
+                              stream=None):
+    """NVFP4 of x^T (blocks of 16 along x's rows) for a 2-D bf16/fp32 CUDA tensor."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    rows, cols = x.shape
+    if out is None:
+        out = NVFP4Tensor(cols, rows, layout, device=x.device)
+    need = nvfp4_workspace_bytes(OP_QUANTIZE, rows, cols, 1 if amax is not None else 0)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    cs = out.c()
+    st = _lib.nvfp4_quantize_transposed(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0),
+                                        _ptr(amax), ctypes.byref(cs), _ptr(workspace),
+                                        workspace.numel() if workspace is not None else 0,
+                                        _stream(stream))
+    _check(st, "nvfp4_quantize_transposed")
     return out
 
 

@@ -94,6 +94,29 @@ int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, i
   return finish();
 }
 
+int nvfp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                              int64_t ld_x, const float* amax, const nvfp4_tensor_t* out,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (rows < 0 || cols < 0) return NVFP4_EINVAL;
+  int st = check_tensor(out);
+  if (st) return st;
+  if (out->rows != cols || out->cols != rows) return NVFP4_ESHAPE;
+  if (cols % 16) return NVFP4_ESHAPE;
+  const int64_t elem = x_dtype == NVFP4_BF16 ? 2 : 4;
+  if (ld_x < cols || (ld_x * elem) % 16) return NVFP4_ESHAPE;
+  if (rows > 0 && cols > 0 && !x) return NVFP4_EINVAL;
+  if (!aligned(x, 16)) return NVFP4_ESHAPE;
+  if (amax && !aligned(amax, 4)) return NVFP4_ESHAPE;
+  const size_t need = nvfp4::quantize_workspace_bytes(rows, cols, amax != nullptr);
+  if (need && (!workspace || ws_bytes < need || !aligned(workspace, 256))) return NVFP4_EWORKSPACE;
+  (void)hipGetLastError();
+  nvfp4::launch_quantize_transposed(x, x_dtype == NVFP4_BF16, rows, cols, ld_x, amax, out->codes,
+                                    out->scales, out->scale_layout == NVFP4_SCALES_TILED,
+                                    out->global_scale, workspace, as_stream(stream));
+  return finish();
+}
+
 int nvfp4_adaln_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
                          int64_t ld_x, const float* shift, const float* scale,
                          int64_t rows_per_group, float eps, float* row_stats,

@@ -23,6 +23,12 @@ void launch_dequantize(const uint8_t* codes, const uint8_t* scales, bool tiled,
                        const float* gscale, int64_t rows, int64_t cols, void* y, bool y_bf16,
                        int64_t ld_y, hipStream_t stream);
 
+// NVFP4 of X^T (blocks along X's rows) into a [cols x rows] tensor (quant.hip);
+// same workspace as launch_quantize.
+void launch_quantize_transposed(const void* x, bool x_bf16, int64_t rows, int64_t cols,
+                                int64_t ld, const float* amax, uint8_t* codes, uint8_t* scales,
+                                bool tiled, float* gscale, void* workspace, hipStream_t stream);
+
 // Fused LayerNorm + adaLN modulate + quantize (quant.hip); row_stats is
 // [rows][2] fp32 (mean, rstd), shift/scale [groups][cols] fp32.
 size_t adaln_quantize_workspace_bytes(int64_t rows, int64_t cols);

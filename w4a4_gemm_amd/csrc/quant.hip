@@ -294,6 +294,111 @@ __global__ __launch_bounds__(256) void dequantize_kernel(
   }
 }
 
+// ------------------------------------------------------------------ transposed quantize
+//
+// NVFP4 of X^T, blocks of 16 along X's rows: the operand layout of the
+// backward GEMMs of NVFP4 training (techwalker.com LongLive-2.0 report
+// summary, sections 一 and 五), where dgrad contracts over a weight's rows and
+// wgrad over the tokens.  A workgroup stages a 128 x 128 tile of X in LDS,
+// row-major with each row's 16-byte chunks XOR-permuted by bits 3..6 of the
+// row, then reads it column-wise: lane l of wave w takes output row
+// k = 32 w + 4 t + l / 16 (a column of X) and the 8 X rows m = 8 (l % 16) + e,
+// the per-lane shape of the plain quantize, so the encoder is shared.  With
+// the permutation, a wave's column reads hit distinct LDS banks (two lanes
+// per dword for bf16).
+
+template <bool kBf16, bool kTiled>
+__global__ __launch_bounds__(256) void quantize_t_kernel(
+    const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+    const float* __restrict__ amax, const float* __restrict__ partial,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gscale) {
+  constexpr int kElem = kBf16 ? 2 : 4;
+  constexpr int kChunks = kTile * kElem / 16;          // 16-byte chunks per tile row
+  constexpr int kPerChunk = 16 / kElem;                // elements per chunk
+  __shared__ u32x4 tile[kTile * kChunks];              // 32 KB (bf16) or 64 KB (fp32)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int64_t m0 = (int64_t)blockIdx.x * kTile;      // X rows of the tile
+  const int64_t k0 = (int64_t)blockIdx.y * kTile;      // X columns of the tile
+  const auto swz = [](int mr, int c) { return c ^ ((mr >> 3) & 15); };
+
+  Partials part;
+  if (!amax) part = load_partials(partial);
+  // stage: rows 32 w + l / 16 + 4 t of the tile, columns 8 j .. 8 j + 7;
+  // out-of-range rows / columns load a valid element and are never stored
+  {
+    const int64_t kc = k0 + 8 * j < cols ? k0 + 8 * j : cols - 8;
+    Raw8 in[kTasks];
+#pragma unroll
+    for (int t = 0; t < kTasks; ++t) {
+      const int64_t m = m0 + 32 * wave + (lane >> 4) + 4 * t;
+      in[t] = load8<kBf16>(x, (m < rows ? m : rows - 1) * ld + kc);
+    }
+#pragma unroll
+    for (int t = 0; t < kTasks; ++t) {
+      const int mr = 32 * wave + (lane >> 4) + 4 * t;
+      if (kBf16) {
+        tile[mr * kChunks + swz(mr, j)] = in[t].a;
+      } else {
+        tile[mr * kChunks + swz(mr, 2 * j)] = in[t].a;
+        tile[mr * kChunks + swz(mr, 2 * j + 1)] = in[t].b;
+      }
+    }
+  }
+  __syncthreads();
+
+  // column reads: task t is output row kr = 32 w + l / 16 + 4 t, X rows 8 j + e
+  Raw8 raw[kTasks];
+#pragma unroll
+  for (int t = 0; t < kTasks; ++t) {
+    const int kr = 32 * wave + (lane >> 4) + 4 * t;
+    const int c = kr / kPerChunk, off = kr % kPerChunk;
+    uint32_t w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int mr = 8 * j + e;
+      const int idx = mr * kChunks + swz(mr, c);
+      if (kBf16)
+        w[e] = ((const uint16_t*)tile)[idx * 8 + off];
+      else
+        w[e] = ((const uint32_t*)tile)[idx * 4 + off];
+    }
+    if (kBf16) {
+      raw[t].a = u32x4{w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16),
+                       w[6] | (w[7] << 16)};
+      raw[t].b = u32x4{0, 0, 0, 0};
+    } else {
+      raw[t].a = u32x4{w[0], w[1], w[2], w[3]};
+      raw[t].b = u32x4{w[4], w[5], w[6], w[7]};
+    }
+  }
+
+  float s_g = global_scale(amax ? *amax : reduce_partials(part));
+  s_g = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_g)));   // uniform
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *gscale = s_g;
+  const TensorEnc te = make_tensor_enc(s_g);
+
+  // the output is [cols x rows]: row k0 + kr, columns m0 + 8 j ..
+  const int64_t orows = cols, ocols = rows;
+  const int64_t r0 = k0 + 32 * wave + (lane >> 4);
+  const int64_t c0 = m0 + 8 * j;
+  const bool cok = c0 < ocols;
+  const int64_t kb = c0 >> 4;
+  uint8_t* cp = codes + r0 * (ocols / 2) + c0 / 2;
+  uint8_t* sp = scales + (kTiled ? ((r0 >> 7) * (ocols / 64) + (kb >> 2)) * 512 +
+                                       (r0 & 127) * 4 + (kb & 3)
+                                 : r0 * (ocols / 16) + kb);
+  const int64_t c_step = 4 * (ocols / 2);
+  const int64_t s_step = kTiled ? 16 : 4 * (ocols / 16);
+  const auto identity = [](int, float*) {};
+  if (te.pre != 1.0f)
+    quantize_tasks<kBf16, kTiled, true>(raw, te, r0, orows, cok, j, cp, sp, c_step, s_step,
+                                        identity);
+  else
+    quantize_tasks<kBf16, kTiled, false>(raw, te, r0, orows, cok, j, cp, sp, c_step, s_step,
+                                         identity);
+}
+
 // ------------------------------------------------------------------ fused LayerNorm + adaLN + quantize
 //
 // The producer of a W4A4 linear's activations in a DiT block: LayerNorm of
@@ -621,6 +726,36 @@ void launch_adaln_quantize(const void* x, bool x_bf16, int64_t rows, int64_t col
                    : go(adaln_quantize_kernel<false, true, false>);
     else two ? go(adaln_quantize_kernel<false, false, true>)
              : go(adaln_quantize_kernel<false, false, false>);
+  }
+}
+
+void launch_quantize_transposed(const void* x, bool x_bf16, int64_t rows, int64_t cols,
+                                int64_t ld, const float* amax, uint8_t* codes, uint8_t* scales,
+                                bool tiled, float* gscale, void* workspace, hipStream_t stream) {
+  float* partial = (float*)workspace;
+  if (!amax) {
+    if (x_bf16)
+      hipLaunchKernelGGL(amax_partial_kernel<true>, dim3(kAmaxPartials), dim3(256), 0, stream,
+                         x, rows, cols, ld, partial);
+    else
+      hipLaunchKernelGGL(amax_partial_kernel<false>, dim3(kAmaxPartials), dim3(256), 0, stream,
+                         x, rows, cols, ld, partial);
+  }
+  if (rows == 0 || cols == 0) {
+    hipLaunchKernelGGL(publish_gscale_kernel, dim3(1), dim3(64), 0, stream, amax, partial, gscale);
+    return;
+  }
+  const dim3 grid((unsigned)((rows + kTile - 1) / kTile), (unsigned)((cols + kTile - 1) / kTile));
+  const auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, x, rows, cols, ld, amax, partial,
+                       codes, scales, gscale);
+  };
+  if (x_bf16) {
+    if (tiled) go(quantize_t_kernel<true, true>);
+    else go(quantize_t_kernel<true, false>);
+  } else {
+    if (tiled) go(quantize_t_kernel<false, true>);
+    else go(quantize_t_kernel<false, false>);
   }
 }
 
