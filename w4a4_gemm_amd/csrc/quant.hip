@@ -22,8 +22,12 @@
 namespace nvfp4 {
 
 namespace {
-constexpr int kTile = 128;         // tile rows and columns
-constexpr int kTasks = 8;          // rows per lane
+#ifndef NVFP4_QUANT_TASKS
+#define NVFP4_QUANT_TASKS 4
+#endif
+constexpr int kTile = 128;                   // tile columns (and rows of the transposed tile)
+constexpr int kTasks = NVFP4_QUANT_TASKS;    // rows per lane
+constexpr int kTileRows = 16 * kTasks;       // rows per workgroup: 4 waves x 4 rows x kTasks
 constexpr int kAmaxUnroll = 8;     // 16-byte loads in flight per lane in the amax pass
 }  // namespace
 
@@ -154,14 +158,14 @@ __global__ __launch_bounds__(64) void publish_gscale_kernel(const float* __restr
 // encoding (a tensor-uniform choice, so the two variants are separate code).
 // `pro(t, v)` maps task t's 8 loaded values to the values that are quantized
 // (the identity for a plain quantize).
-template <bool kBf16, bool kTiled, bool kPre, typename Prologue>
+template <int kN, bool kBf16, bool kTiled, bool kPre, typename Prologue>
 __device__ __forceinline__ void quantize_tasks(const Raw8* raw, const TensorEnc& te, int64_t r0,
                                                int64_t rows, bool cok, int j,
                                                uint8_t* __restrict__ cp,
                                                uint8_t* __restrict__ sp, int64_t c_step,
                                                int64_t s_step, const Prologue& pro) {
 #pragma unroll
-  for (int t = 0; t < kTasks; ++t) {
+  for (int t = 0; t < kN; ++t) {
     float v[8];
     unpack8<kBf16>(raw[t], v);
     pro(t, v);
@@ -191,7 +195,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15;
   const int64_t c0 = (int64_t)blockIdx.y * kTile + 8 * j;
-  const int64_t r0 = (int64_t)blockIdx.x * kTile + 32 * wave + (lane >> 4);
+  const int64_t r0 = (int64_t)blockIdx.x * kTileRows + 4 * kTasks * wave + (lane >> 4);
   const bool cok = c0 < cols;
 
   // partial maxima first: in-order completion then lets task 0 start as soon
@@ -222,10 +226,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(
   const int64_t s_step = kTiled ? 16 : 4 * (cols / 16);   // tiled: 128-row tiles hold all 8 tasks
   const auto identity = [](int, float*) {};
   if (te.pre != 1.0f)
-    quantize_tasks<kBf16, kTiled, true>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
+    quantize_tasks<kTasks, kBf16, kTiled, true>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
                                         identity);
   else
-    quantize_tasks<kBf16, kTiled, false>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
+    quantize_tasks<kTasks, kBf16, kTiled, false>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
                                          identity);
 }
 
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(256) void dequantize_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15;
   const int64_t c0 = (int64_t)blockIdx.y * kTile + 8 * j;
-  const int64_t r0 = (int64_t)blockIdx.x * kTile + 32 * wave + (lane >> 4);
+  const int64_t r0 = (int64_t)blockIdx.x * kTileRows + 4 * kTasks * wave + (lane >> 4);
   if (c0 >= cols) return;
 
   uint32_t cw[kTasks], sbyte[kTasks];
@@ -312,6 +316,7 @@ __global__ __launch_bounds__(256) void quantize_t_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     const float* __restrict__ amax, const float* __restrict__ partial,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gscale) {
+  constexpr int kTT = kTile / 16;                      // rows per lane (128-row tile)
   constexpr int kElem = kBf16 ? 2 : 4;
   constexpr int kChunks = kTile * kElem / 16;          // 16-byte chunks per tile row
   constexpr int kPerChunk = 16 / kElem;                // elements per chunk
@@ -328,14 +333,14 @@ __global__ __launch_bounds__(256) void quantize_t_kernel(
   // out-of-range rows / columns load a valid element and are never stored
   {
     const int64_t kc = k0 + 8 * j < cols ? k0 + 8 * j : cols - 8;
-    Raw8 in[kTasks];
+    Raw8 in[kTT];
 #pragma unroll
-    for (int t = 0; t < kTasks; ++t) {
+    for (int t = 0; t < kTT; ++t) {
       const int64_t m = m0 + 32 * wave + (lane >> 4) + 4 * t;
       in[t] = load8<kBf16>(x, (m < rows ? m : rows - 1) * ld + kc);
     }
 #pragma unroll
-    for (int t = 0; t < kTasks; ++t) {
+    for (int t = 0; t < kTT; ++t) {
       const int mr = 32 * wave + (lane >> 4) + 4 * t;
       if (kBf16) {
         tile[mr * kChunks + swz(mr, j)] = in[t].a;
@@ -348,9 +353,9 @@ __global__ __launch_bounds__(256) void quantize_t_kernel(
   __syncthreads();
 
   // column reads: task t is output row kr = 32 w + l / 16 + 4 t, X rows 8 j + e
-  Raw8 raw[kTasks];
+  Raw8 raw[kTT];
 #pragma unroll
-  for (int t = 0; t < kTasks; ++t) {
+  for (int t = 0; t < kTT; ++t) {
     const int kr = 32 * wave + (lane >> 4) + 4 * t;
     const int c = kr / kPerChunk, off = kr % kPerChunk;
     uint32_t w[8];
@@ -392,10 +397,10 @@ __global__ __launch_bounds__(256) void quantize_t_kernel(
   const int64_t s_step = kTiled ? 16 : 4 * (ocols / 16);
   const auto identity = [](int, float*) {};
   if (te.pre != 1.0f)
-    quantize_tasks<kBf16, kTiled, true>(raw, te, r0, orows, cok, j, cp, sp, c_step, s_step,
+    quantize_tasks<kTT, kBf16, kTiled, true>(raw, te, r0, orows, cok, j, cp, sp, c_step, s_step,
                                         identity);
   else
-    quantize_tasks<kBf16, kTiled, false>(raw, te, r0, orows, cok, j, cp, sp, c_step, s_step,
+    quantize_tasks<kTT, kBf16, kTiled, false>(raw, te, r0, orows, cok, j, cp, sp, c_step, s_step,
                                          identity);
 }
 
@@ -450,15 +455,28 @@ __device__ __forceinline__ void load_f32(const float* __restrict__ p, float* v, 
 }
 
 constexpr int kStatRegChunks = 8;   // 16-byte chunks of a row a lane keeps in registers
+constexpr int64_t kModLdsBytes = 64 * 1024;   // LDS for one group's gain and shift vectors
 
-// One wave, one row: statistics (fp64 sums; mean and rstd rounded once to
-// fp32), stored by lane 0; returns this lane's max |x'|.  kRegs: the row
-// (at most 64 kStatRegChunks chunks) stays in registers across the three
-// sweeps; otherwise each sweep reads it again (from cache).
-template <bool kBf16, bool kRegs>
+__device__ __forceinline__ void wave_sum2(double& a, double& b) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    a += __shfl_xor(a, o);
+    b += __shfl_xor(b, o);
+  }
+}
+
+// One wave, one row: statistics, stored by lane 0; returns this lane's max |x'|.
+// The sums run in fp64 about a pivot p (the row's first element):
+// s1 = sum (x - p), s2 = sum (x - p)^2, mean = p + s1 / n, var = s2 / n - (s1 / n)^2.
+// (p - mean)^2 <= n var, so the subtraction loses at most log2(n) of fp64's
+// 53 bits.  mean and rstd are rounded once to fp32.  kRegs: the row (at most
+// 64 kStatRegChunks chunks) stays in registers for the modulate sweep;
+// otherwise that sweep reads it again (from cache).  kLds: gain (= 1 + scale)
+// and shift come from LDS, else from global memory.
+template <bool kBf16, bool kRegs, bool kLds>
 __device__ __forceinline__ float adaln_row(const u32x4* __restrict__ xr, int64_t cpr,
-                                           int64_t cols, const float* __restrict__ sh,
-                                           const float* __restrict__ sc, float eps, int lane,
+                                           int64_t cols, const float* gain_or_scale,
+                                           const float* shift, float eps, int lane,
                                            float2* __restrict__ st) {
   constexpr int kPer = kBf16 ? 8 : 4;
   constexpr int kU = kRegs ? kStatRegChunks : 1;
@@ -489,60 +507,95 @@ __device__ __forceinline__ float adaln_row(const u32x4* __restrict__ xr, int64_t
       }
     }
   };
-  double s = 0.0;
-  for_chunks([&](int64_t, const float* v) {
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) s += (double)v[e];
-  });
-  const double mean = wave_sum(s) / (double)cols;
-  double q = 0.0;
+  const uint32_t first = kRegs ? w[0][0] : xr[0][0];
+  const double p = kBf16 ? (double)bf16_lo(__builtin_amdgcn_readfirstlane(first))
+                         : (double)__uint_as_float(__builtin_amdgcn_readfirstlane(first));
+  double s1 = 0.0, s2 = 0.0;
   for_chunks([&](int64_t, const float* v) {
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-      const double d = (double)v[e] - mean;
-      q += d * d;
+      const double d = (double)v[e] - p;
+      s1 += d;
+      s2 = __builtin_fma(d, d, s2);
     }
   });
-  const double var = wave_sum(q) / (double)cols;
-  const float mu = (float)mean;
+  wave_sum2(s1, s2);
+  const double a1 = s1 / (double)cols;
+  const double var = fmax(s2 / (double)cols - a1 * a1, 0.0);
+  const float mu = (float)(p + a1);
   const float rstd = (float)(1.0 / sqrt(var + (double)eps));
   float m = 0.0f;
   for_chunks([&](int64_t i, const float* v) {
-    float shv[kPer], scv[kPer];
-    load_f32(sh + i * kPer, shv, kPer);
-    load_f32(sc + i * kPer, scv, kPer);
+    float gv[kPer], shv[kPer];
+    if (kLds) {
+#pragma unroll
+      for (int k = 0; k < kPer / 4; ++k) {
+        const f32x4 a = *(const f32x4*)(gain_or_scale + i * kPer + 4 * k);
+        const f32x4 b = *(const f32x4*)(shift + i * kPer + 4 * k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          gv[4 * k + e] = a[e];
+          shv[4 * k + e] = b[e];
+        }
+      }
+    } else {
+      load_f32(gain_or_scale + i * kPer, gv, kPer);
+      load_f32(shift + i * kPer, shv, kPer);
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) gv[e] = 1.0f + gv[e];
+    }
 #pragma unroll
     for (int e = 0; e < kPer; ++e)
-      m = fmaxf(m, __builtin_fabsf(adaln_value(v[e], mu, rstd, 1.0f + scv[e], shv[e])));
+      m = fmaxf(m, __builtin_fabsf(adaln_value(v[e], mu, rstd, gv[e], shv[e])));
   });
   if (lane == 0) *st = make_float2(mu, rstd);
   return m;
 }
 
-// Stats pass: wave w of workgroup b takes rows 4 b + w, 4 b + w + 4 G, ...
-// (G workgroups); every workgroup writes its partial max |x'| (0 if idle).
-template <bool kBf16>
+// Stats pass: workgroup b takes the band of rows [b B, b B + B) and walks it
+// one modulation group at a time (kLds: the group's gain and shift vectors are
+// staged in LDS once, 8 cols bytes); its 4 waves take the group's rows in
+// turn.  Every workgroup writes its partial max |x'| (0 if idle).
+template <bool kBf16, bool kLds>
 __global__ __launch_bounds__(256) void adaln_stats_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     const float* __restrict__ shift, const float* __restrict__ scale, int64_t rpg, float eps,
-    float2* __restrict__ stats, float* __restrict__ partial) {
-  const int lane = threadIdx.x & 63;
+    int64_t band, float2* __restrict__ stats, float* __restrict__ partial) {
+  extern __shared__ f32x4 mod4[];                 // kLds: gain [cols] then shift [cols]
+  float* mod = (float*)mod4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t cpr = cols / (kBf16 ? 8 : 4);
-  const int64_t nw = (int64_t)gridDim.x * 4;
+  const int64_t b0 = (int64_t)blockIdx.x * band;
+  const int64_t b1 = b0 + band < rows ? b0 + band : rows;
   float m = 0.0f;
-  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows; r += nw) {
-    const u32x4* xr = (const u32x4*)((const char*)x + r * ld * (kBf16 ? 2 : 4));
-    const int64_t g = r / rpg;
-    if (cpr <= 64 * kStatRegChunks)
-      m = fmaxf(m, adaln_row<kBf16, true>(xr, cpr, cols, shift + g * cols, scale + g * cols, eps,
-                                          lane, stats + r));
-    else
-      m = fmaxf(m, adaln_row<kBf16, false>(xr, cpr, cols, shift + g * cols, scale + g * cols,
-                                           eps, lane, stats + r));
+  for (int64_t g0 = b0; g0 < b1;) {               // uniform over the workgroup
+    const int64_t g = g0 / rpg;
+    const int64_t g1 = (g + 1) * rpg < b1 ? (g + 1) * rpg : b1;
+    const float* sc = scale + g * cols;
+    const float* sh = shift + g * cols;
+    if (kLds) {
+      __syncthreads();                            // readers of the previous group are done
+      for (int64_t i = threadIdx.x; i < cols / 4; i += 256) {
+        const f32x4 a = ((const f32x4*)sc)[i];
+        mod4[i] = f32x4{1.0f + a[0], 1.0f + a[1], 1.0f + a[2], 1.0f + a[3]};
+        mod4[cols / 4 + i] = ((const f32x4*)sh)[i];
+      }
+      __syncthreads();
+    }
+    for (int64_t r = g0 + wave; r < g1; r += 4) {
+      const u32x4* xr = (const u32x4*)((const char*)x + r * ld * (kBf16 ? 2 : 4));
+      const float* gs = kLds ? mod : sc;
+      const float* shp = kLds ? mod + cols : sh;
+      if (cpr <= 64 * kStatRegChunks)
+        m = fmaxf(m, adaln_row<kBf16, true, kLds>(xr, cpr, cols, gs, shp, eps, lane, stats + r));
+      else
+        m = fmaxf(m, adaln_row<kBf16, false, kLds>(xr, cpr, cols, gs, shp, eps, lane, stats + r));
+    }
+    g0 = g1;
   }
   m = wave_max(m);
   __shared__ float red[4];
-  if (lane == 0) red[threadIdx.x >> 6] = m;
+  if (lane == 0) red[wave] = m;
   __syncthreads();
   if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
@@ -560,7 +613,7 @@ __global__ __launch_bounds__(256) void adaln_quantize_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15;
   const int64_t c0 = (int64_t)blockIdx.y * kTile + 8 * j;
-  const int64_t r0 = (int64_t)blockIdx.x * kTile + 32 * wave + (lane >> 4);
+  const int64_t r0 = (int64_t)blockIdx.x * kTileRows + 4 * kTasks * wave + (lane >> 4);
   const bool cok = c0 < cols;
 
   const Partials part = load_partials(partial);
@@ -621,10 +674,10 @@ __global__ __launch_bounds__(256) void adaln_quantize_kernel(
   const int64_t c_step = 4 * (cols / 2);
   const int64_t s_step = kTiled ? 16 : 4 * (cols / 16);
   if (te.pre != 1.0f)
-    quantize_tasks<kBf16, kTiled, true>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
+    quantize_tasks<kTasks, kBf16, kTiled, true>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
                                         modulate);
   else
-    quantize_tasks<kBf16, kTiled, false>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
+    quantize_tasks<kTasks, kBf16, kTiled, false>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
                                          modulate);
 }
 
@@ -649,7 +702,8 @@ void launch_quantize(const void* x, bool x_bf16, int64_t rows, int64_t cols, int
       hipLaunchKernelGGL(amax_partial_kernel<false>, dim3(kAmaxPartials), dim3(256), 0, stream,
                          x, rows, cols, ld, partial);
   }
-  const dim3 grid((unsigned)((rows + kTile - 1) / kTile), (unsigned)((cols + kTile - 1) / kTile));
+  const dim3 grid((unsigned)((rows + kTileRows - 1) / kTileRows),
+                  (unsigned)((cols + kTile - 1) / kTile));
   if (rows == 0 || cols == 0) {
     hipLaunchKernelGGL(publish_gscale_kernel, dim3(1), dim3(64), 0, stream, amax, partial, gscale);
     return;
@@ -671,7 +725,8 @@ void launch_dequantize(const uint8_t* codes, const uint8_t* scales, bool tiled,
                        const float* gscale, int64_t rows, int64_t cols, void* y, bool y_bf16,
                        int64_t ld_y, hipStream_t stream) {
   if (rows == 0 || cols == 0) return;
-  const dim3 grid((unsigned)((rows + kTile - 1) / kTile), (unsigned)((cols + kTile - 1) / kTile));
+  const dim3 grid((unsigned)((rows + kTileRows - 1) / kTileRows),
+                  (unsigned)((cols + kTile - 1) / kTile));
 #define NVFP4_DLAUNCH(T, B)                                                                  \
   hipLaunchKernelGGL((dequantize_kernel<T, B>), grid, dim3(256), 0, stream, codes, scales,   \
                      gscale, rows, cols, y, ld_y)
@@ -697,20 +752,29 @@ void launch_adaln_quantize(const void* x, bool x_bf16, int64_t rows, int64_t col
                            bool tiled, float* gscale, void* workspace, hipStream_t stream) {
   float* partial = (float*)workspace;
   float2* stats = (float2*)row_stats;
-  // cols == 0: no row has statistics; only s_g (1) is published
+  // cols == 0: no row has statistics; only s_g (1) is published.  Rows are
+  // dealt in contiguous bands, one per workgroup (all kAmaxPartials write).
   const int64_t srows = cols > 0 ? rows : 0;
-  if (x_bf16)
-    hipLaunchKernelGGL(adaln_stats_kernel<true>, dim3(kAmaxPartials), dim3(256), 0, stream, x,
-                       srows, cols, ld, shift, scale, rows_per_group, eps, stats, partial);
-  else
-    hipLaunchKernelGGL(adaln_stats_kernel<false>, dim3(kAmaxPartials), dim3(256), 0, stream, x,
-                       srows, cols, ld, shift, scale, rows_per_group, eps, stats, partial);
+  const int64_t band = srows > 0 ? (srows + kAmaxPartials - 1) / kAmaxPartials : 1;
+  const size_t lds = (size_t)cols * 8;
+  const auto stats_go = [&](auto kernel, size_t bytes) {
+    hipLaunchKernelGGL(kernel, dim3(kAmaxPartials), dim3(256), bytes, stream, x, srows, cols, ld,
+                       shift, scale, rows_per_group, eps, band, stats, partial);
+  };
+  if (lds <= (size_t)kModLdsBytes) {
+    if (x_bf16) stats_go(adaln_stats_kernel<true, true>, lds);
+    else stats_go(adaln_stats_kernel<false, true>, lds);
+  } else {
+    if (x_bf16) stats_go(adaln_stats_kernel<true, false>, 0);
+    else stats_go(adaln_stats_kernel<false, false>, 0);
+  }
   if (rows == 0 || cols == 0) {
     hipLaunchKernelGGL(publish_gscale_kernel, dim3(1), dim3(64), 0, stream, nullptr, partial,
                        gscale);
     return;
   }
-  const dim3 grid((unsigned)((rows + kTile - 1) / kTile), (unsigned)((cols + kTile - 1) / kTile));
+  const dim3 grid((unsigned)((rows + kTileRows - 1) / kTileRows),
+                  (unsigned)((cols + kTile - 1) / kTile));
   const bool two = rows_per_group > 4 * (kTasks - 1);
   const auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, x, rows, cols, ld, shift, scale,
