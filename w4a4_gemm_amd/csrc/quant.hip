@@ -7,14 +7,14 @@
 // the E2M1 codes in registers (the fused scale+quantize kernel the
 // ai-manual.ru article credits with a 20% saving).
 //
-// Layout of work (quantize and dequantize): a workgroup covers a tile of 128
-// rows x 128 columns.  Lane l of wave w owns 8 consecutive values, column
-// chunk j = l % 16 of the tile, in rows 32 w + 4 t + l / 16 for t = 0..7.  A
-// wave's load instruction therefore reads 4 rows x 256 contiguous bytes (bf16),
-// two neighbouring lanes form one 16-value block (the even one stores its
-// scale byte), a lane's 8 codes are one dword (16 lanes store a row's 64
-// contiguous bytes), and the workgroup writes both 512-byte tiles of the tiled
-// scale layout that its 128 rows touch.
+// Layout of work (quantize and dequantize): a workgroup covers a tile of
+// 16 kTasks rows x 128 columns.  Lane l of wave w owns 8 consecutive values,
+// column chunk j = l % 16 of the tile, in rows 4 kTasks w + 4 t + l / 16 for
+// t < kTasks.  A wave's load instruction therefore reads 4 rows x 256
+// contiguous bytes (bf16), two neighbouring lanes form one 16-value block (the
+// even one stores its scale byte), a lane's 8 codes are one dword (16 lanes
+// store a row's 64 contiguous bytes), and the workgroup's rows lie inside one
+// 128-row band of the tiled scale layout.
 
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
                                        (r0 & 127) * 4 + (kb & 3)
                                  : r0 * (cols / 16) + kb);
   const int64_t c_step = 4 * (cols / 2);
-  const int64_t s_step = kTiled ? 16 : 4 * (cols / 16);   // tiled: 128-row tiles hold all 8 tasks
+  const int64_t s_step = kTiled ? 16 : 4 * (cols / 16);   // tiled: a 128-row band holds every task
   const auto identity = [](int, float*) {};
   if (te.pre != 1.0f)
     quantize_tasks<kTasks, kBf16, kTiled, true>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
