@@ -46,6 +46,7 @@ struct PageInfo {
   int split;              // slots [0, split) belong to chunk c0, the rest to c1
   int c0, c1;
   float sgk0, sgk1, sgv0, sgv1;
+  bool vcheck;            // a V^ product of this page may need the bf16 midpoint fix-up
 };
 
 __device__ __forceinline__ PageInfo page_info(const KvGeom& g, int64_t n_phys,
@@ -68,16 +69,18 @@ __device__ __forceinline__ PageInfo page_info(const KvGeom& g, int64_t n_phys,
   p.sgk1 = g.k_gscale[p.c1];
   p.sgv0 = g.v_gscale[p.c0];
   p.sgv1 = g.v_gscale[p.c1];
+  p.vcheck = product_needs_check(p.sgv0) || product_needs_check(p.sgv1);
   return p;
 }
 
 // The raw inputs of one block for this thread: its units are the 4 adjacent
 // keys 4 (tid / 16) + i (i = 0..3) in channel group tid % 16 (the same 8
-// channels for every unit), so the thread needs the K means of those 8
-// channels for the page's two chunks, and writes V^T as 4-key runs.
+// channels for every unit), written to V^T as 4-key runs.  The K means of the
+// page's two chunks (2 x 128 floats) travel one per thread and are shared
+// through LDS.
 struct BlockRaw {
   uint32_t kc[4], ks[4], vc[4], vs[4];
-  f32x4 mu0a, mu0b, mu1a, mu1b;
+  float mu;               // K mean of chunk (tid < 128 ? c0 : c1), channel tid % 128
 };
 
 __device__ __forceinline__ void fetch_block(const KvGeom& g, const PageInfo& p, int h, int s0,
@@ -95,25 +98,22 @@ __device__ __forceinline__ void fetch_block(const KvGeom& g, const PageInfo& p, 
     r.vc[i] = *(const uint32_t*)(p.page + codes_region + scales_region + row * (kD / 2) + 4 * sub);
     r.vs[i] = p.page[2 * codes_region + scales_region + row * (kD / 16) + (sub >> 1)];
   }
-  const float* m0 = g.k_mean + ((int64_t)p.c0 * H + h) * kD + 8 * sub;
-  const float* m1 = g.k_mean + ((int64_t)p.c1 * H + h) * kD + 8 * sub;
-  r.mu0a = *(const f32x4*)m0;
-  r.mu0b = *(const f32x4*)(m0 + 4);
-  r.mu1a = *(const f32x4*)m1;
-  r.mu1b = *(const f32x4*)(m1 + 4);
+  r.mu = g.k_mean[((int64_t)(threadIdx.x < kD ? p.c0 : p.c1) * H + h) * kD + (threadIdx.x & (kD - 1))];
 }
 
-// Decode a fetched block into K^ rows and V^T columns of LDS (unmapped pages
-// give zeros; such keys are masked anyway).
+// Decode a fetched block into K^ rows and V^T columns of LDS.  Slots that hold
+// no key (unmapped page, past the last valid slot) give zeros: their weights are
+// 0, and zero values keep 0 * V^ finite whatever bytes the slot holds.
 template <bool kVCheck>
 __device__ __forceinline__ void decode_block(const PageInfo& p, int s0, const BlockRaw& r,
+                                             const float* __restrict__ Mu,
                                              uint16_t* __restrict__ Ks,
                                              uint16_t* __restrict__ Vt) {
   const int sub = threadIdx.x & 15;
-  const float mu0[8] = {r.mu0a[0], r.mu0a[1], r.mu0a[2], r.mu0a[3],
-                        r.mu0b[0], r.mu0b[1], r.mu0b[2], r.mu0b[3]};
-  const float mu1[8] = {r.mu1a[0], r.mu1a[1], r.mu1a[2], r.mu1a[3],
-                        r.mu1b[0], r.mu1b[1], r.mu1b[2], r.mu1b[3]};
+  const f32x4 a0 = *(const f32x4*)(Mu + 8 * sub), b0 = *(const f32x4*)(Mu + 8 * sub + 4);
+  const f32x4 a1 = *(const f32x4*)(Mu + kD + 8 * sub), b1 = *(const f32x4*)(Mu + kD + 8 * sub + 4);
+  const float mu0[8] = {a0[0], a0[1], a0[2], a0[3], b0[0], b0[1], b0[2], b0[3]};
+  const float mu1[8] = {a1[0], a1[1], a1[2], a1[3], b1[0], b1[1], b1[2], b1[3]};
   uint32_t vw[4][4];                                        // V^ words of the 4 keys
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -122,7 +122,7 @@ __device__ __forceinline__ void decode_block(const PageInfo& p, int s0, const Bl
     u32x4 ko, vo;
     kv_unit_bf16<kVCheck>(r.kc[i], r.ks[i], r.vc[i], r.vs[i], second ? p.sgk1 : p.sgk0,
                           second ? p.sgv1 : p.sgv0, second ? mu1 : mu0, ko, vo);
-    if (!p.mapped) {
+    if (!p.mapped || s0 + key >= p.valid) {               // no key here: zeros, never NaN
       ko = u32x4{0, 0, 0, 0};
       vo = u32x4{0, 0, 0, 0};
     }
@@ -169,15 +169,19 @@ size_t kv_attention_workspace_bytes(int64_t n_q, int64_t n_heads, int64_t n_keys
 // unnormalized fp32 O^T, the running max m (log2 units) and the sum l go to
 // the workspace: O at part + ((split * n_q + n) * H + h) * D, (m, l) after all
 // O values.
-__global__ __launch_bounds__(256) void kv_attention_kernel(KvGeom g, int64_t n_phys,
+// Two workgroups per CU (registers capped at 256 per lane), so one
+// workgroup's decode overlaps the other's MFMAs.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void kv_attention_kernel(KvGeom g, int64_t n_phys,
                                                            const int32_t* __restrict__ pages,
                                                            int n_pages, int last_tokens,
                                                            const uint16_t* __restrict__ q,
                                                            int64_t n_q, float scale_log2e,
+                                                           uint32_t q_sign,
                                                            uint16_t* __restrict__ out,
                                                            float* __restrict__ part, int n_split) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kKB * kKsRow];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[kD * kVtRow];
+  __shared__ __attribute__((aligned(16))) float Mu[2 * kD];    // K means: chunk c0, then c1
   const int H = g.n_heads, P = g.page_tokens;
   const int h = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -191,7 +195,11 @@ __global__ __launch_bounds__(256) void kv_attention_kernel(KvGeom g, int64_t n_p
   {
     const uint16_t* qp = q + (qn * H + h) * kD + 8 * half;
 #pragma unroll
-    for (int s = 0; s < kD / 16; ++s) qf[s] = *(const u32x4*)(qp + 16 * s);
+    for (int s = 0; s < kD / 16; ++s) {
+      qf[s] = *(const u32x4*)(qp + 16 * s);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf[s][e] ^= q_sign;       // -q when the scale is negative
+    }
   }
   f32x16 o[kD / 32];
 #pragma unroll
@@ -221,11 +229,12 @@ __global__ __launch_bounds__(256) void kv_attention_kernel(KvGeom g, int64_t n_p
       fetch_block(g, pn, h, ((b + 1) % bpp) * kKB, rn);
     }
     if (pc.valid <= s0) continue;                           // whole block masked (uniform)
-    __syncthreads();                                        // previous block's LDS reads done
-    if (product_needs_check(pc.sgv0) || product_needs_check(pc.sgv1))
-      decode_block<true>(pc, s0, rc, Ks, Vt);
+    Mu[tid] = rc.mu;                       // safe: the previous decode's reads of Mu
+    __syncthreads();                       // finished before the previous block's MFMAs
+    if (pc.vcheck)
+      decode_block<true>(pc, s0, rc, Mu, Ks, Vt);
     else
-      decode_block<false>(pc, s0, rc, Ks, Vt);
+      decode_block<false>(pc, s0, rc, Mu, Ks, Vt);
     __syncthreads();
 
     // S^T tiles: keys 32 kt + (r / 4) * 8 + 4 half + r % 4 of this block, query lane % 32
@@ -240,36 +249,42 @@ __global__ __launch_bounds__(256) void kv_attention_kernel(KvGeom g, int64_t n_p
         st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*(const u32x4*)(kp + 16 * s)),
                                                          as_bf16x8(qf[s]), st[kt], 0, 0, 0);
     }
-    // online softmax for this lane's query (keys split between lane and lane ^ 32)
+    // online softmax for this lane's query (keys split between lane and lane ^ 32),
+    // in log2 units: t = S c with c = |scale| log2(e) >= 0, so the block max of t is
+    // RN(c max S) and each weight is exp2(fma(S, c, -m)).  Keys past the last
+    // valid slot only occur in a block that is not full (uniform test).
+    const bool full = s0 + kKB <= pc.valid;
     float mb = -__builtin_inff();
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 32 * kt + (r >> 2) * 8 + 4 * half + (r & 3);
-        const float t = s0 + key < pc.valid ? st[kt][r] * scale_log2e : -__builtin_inff();
-        st[kt][r] = t;
-        mb = fmaxf(mb, t);
+        if (full || s0 + key < pc.valid) mb = fmaxf(mb, st[kt][r]);
       }
     mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    const float m_new = fmaxf(m, mb);                       // finite: the block has a valid key
+    const float m_new = fmaxf(m, mb * scale_log2e);         // finite: the block has a valid key
     const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first block
     float ps = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(st[kt][r] - m_new);
+        const int key = 32 * kt + (r >> 2) * 8 + 4 * half + (r & 3);
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kt][r], scale_log2e, -m_new));
+        if (!full && s0 + key >= pc.valid) p = 0.0f;
         st[kt][r] = p;
         ps += p;
       }
     ps += __shfl_xor(ps, 32, 64);
     l = l * alpha + ps;
     m = m_new;
+    if (__any(alpha != 1.0f)) {                             // the running max moved
 #pragma unroll
-    for (int dt = 0; dt < kD / 32; ++dt)
+      for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
 
     // O^T += V^T P^T.  Step kk of key tile kt: k index j of lane half `half` is
     // key 32 kt + 16 kk + (j / 4) * 8 + 4 half + j % 4 = S^T register 8 kk + j.
@@ -350,11 +365,14 @@ void launch_kv_attention(const KvGeom& g, const int32_t* logical_pages, int32_t 
                          int32_t last_page_tokens, const uint16_t* q, int64_t n_q,
                          float softmax_scale, uint16_t* out, void* workspace,
                          hipStream_t stream) {
-  const float scale_log2e = (float)((double)softmax_scale * 1.4426950408889634);
+  // logits in log2 units with a non-negative factor; a negative scale negates q
+  // instead (exact in bf16), so the block max maps to the max weight
+  const float scale_log2e = (float)(fabs((double)softmax_scale) * 1.4426950408889634);
+  const uint32_t q_sign = softmax_scale < 0.0f ? 0x80008000u : 0u;
   const int n_split = attention_splits(n_q, g.n_heads, (int64_t)n_pages * g.page_tokens);
   const dim3 grid((unsigned)((n_q + kQB - 1) / kQB), (unsigned)g.n_heads, (unsigned)n_split);
   hipLaunchKernelGGL(kv_attention_kernel, grid, dim3(256), 0, stream, g, g.n_phys_pages,
-                     logical_pages, n_pages, last_page_tokens, q, n_q, scale_log2e, out,
+                     logical_pages, n_pages, last_page_tokens, q, n_q, scale_log2e, q_sign, out,
                      (float*)workspace, n_split);
   if (n_split > 1) {
     const int64_t rows = n_q * g.n_heads;
