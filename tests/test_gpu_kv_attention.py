@@ -118,3 +118,14 @@ def test_split_window_with_an_empty_split():
     _write(gpu, ora, 0, kb, vb, 10 * p)                     # logical pages 10..19
     qb = synth.attn_queries(50, h, 128, seed=101)
     _check(gpu, ora, list(range(20)), p, qb, 1 / math.sqrt(128), 10)
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0])
+def test_negative_and_zero_scale(scale):
+    # a negative scale prefers the keys least aligned with q; scale 0 averages V^
+    h, p = 2, 64
+    gpu, ora = _pair(h, p, 6, 1, np.array([[4, 1, 5, 0, 2, 3]], dtype=np.int32), 6)
+    kb, vb = synth.kv_chunk(t=330, h=h, d=128, seed_k=102, seed_v=103, seed_off=104)
+    _write(gpu, ora, 0, kb, vb, 0)
+    qb = synth.attn_queries(40, h, 128, seed=105)
+    _check(gpu, ora, [0, 1, 2, 3, 4, 5], 330 - 5 * p, qb, scale, 6)

@@ -31,10 +31,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kD = 128;               // head_dim
-constexpr int kQB = 128;              // queries per workgroup
+#ifndef NVFP4_ATTN_WAVES
+#define NVFP4_ATTN_WAVES 4
+#endif
+constexpr int kWaves = NVFP4_ATTN_WAVES;  // waves per workgroup, 32 queries each
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQB = 32 * kWaves;          // queries per workgroup
+constexpr int kKPT = 64 * 16 / kThreads;  // keys per thread in a block's decode
 constexpr int kKB = 64;               // keys per block
 constexpr int kKsRow = kD + 8;        // bf16 per K^ row in LDS (272 bytes: conflict-free reads)
 constexpr int kVtRow = kKB + 8;       // bf16 per V^T row in LDS (144 bytes)
+constexpr size_t kAttnLds =           // Q rows + K^ rows + V^T rows + K means (71,680 bytes)
+    2 * ((size_t)kQB * kKsRow + (size_t)kKB * kKsRow + (size_t)kD * kVtRow) + 2 * kD * 4;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -79,52 +87,69 @@ __device__ __forceinline__ PageInfo page_info(const KvGeom& g, int64_t n_phys,
 // page's two chunks (2 x 128 floats) travel one per thread and are shared
 // through LDS.
 struct BlockRaw {
-  uint32_t kc[4], ks[4], vc[4], vs[4];
-  float mu;               // K mean of chunk (tid < 128 ? c0 : c1), channel tid % 128
+  uint32_t kc[kKPT], ks[kKPT], vc[kKPT], vs[kKPT];
+  float mu;               // K mean of chunk (tid < 128 ? c0 : c1), channel tid % 128 (tid < 256)
 };
 
 __device__ __forceinline__ void fetch_block(const KvGeom& g, const PageInfo& p, int h, int s0,
                                             BlockRaw& r) {
-  const int H = g.n_heads, P = g.page_tokens;
-  const int64_t codes_region = (int64_t)H * P * (kD / 2);
-  const int64_t scales_region = (int64_t)H * P * (kD / 16);
-  const int sub = threadIdx.x & 15;
+  // 32-bit offsets from the (uniform) page address: a page is far below 4 GiB
+  const uint32_t H = g.n_heads, P = g.page_tokens;
+  const uint32_t codes_region = H * P * (kD / 2);
+  const uint32_t scales_region = H * P * (kD / 16);
+  const uint32_t sub = threadIdx.x & 15;
+  const uint32_t row0 = (uint32_t)h * P + s0 + kKPT * (threadIdx.x >> 4);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = 4 * (threadIdx.x >> 4) + i;
-    const int64_t row = (int64_t)h * P + s0 + key;
-    r.kc[i] = *(const uint32_t*)(p.page + row * (kD / 2) + 4 * sub);
+  for (int i = 0; i < kKPT; ++i) {
+    const uint32_t row = row0 + i;
+    r.kc[i] = *(const uint32_t*)(p.page + (row * (kD / 2) + 4 * sub));
     r.ks[i] = p.page[codes_region + row * (kD / 16) + (sub >> 1)];
-    r.vc[i] = *(const uint32_t*)(p.page + codes_region + scales_region + row * (kD / 2) + 4 * sub);
+    r.vc[i] = *(const uint32_t*)(p.page + (codes_region + scales_region + row * (kD / 2) + 4 * sub));
     r.vs[i] = p.page[2 * codes_region + scales_region + row * (kD / 16) + (sub >> 1)];
   }
-  r.mu = g.k_mean[((int64_t)(threadIdx.x < kD ? p.c0 : p.c1) * H + h) * kD + (threadIdx.x & (kD - 1))];
+  if (threadIdx.x < 2 * kD)
+    r.mu = g.k_mean[((int64_t)(threadIdx.x < kD ? p.c0 : p.c1) * H + h) * kD + (threadIdx.x & (kD - 1))];
 }
 
 // Decode a fetched block into K^ rows and V^T columns of LDS.  Slots that hold
 // no key (unmapped page, past the last valid slot) give zeros: their weights are
 // 0, and zero values keep 0 * V^ finite whatever bytes the slot holds.
-template <bool kVCheck>
-__device__ __forceinline__ void decode_block(const PageInfo& p, int s0, const BlockRaw& r,
-                                             const float* __restrict__ Mu,
+// kSimple: the block is mapped, every slot holds a key and all belong to chunk
+// `cs` (uniform), so no per-key choice of chunk or mask is needed.
+template <bool kVCheck, bool kSimple>
+__device__ __forceinline__ void decode_block(const PageInfo& p, int s0, int cs,
+                                             const BlockRaw& r, const float* __restrict__ Mu,
                                              uint16_t* __restrict__ Ks,
                                              uint16_t* __restrict__ Vt) {
   const int sub = threadIdx.x & 15;
-  const f32x4 a0 = *(const f32x4*)(Mu + 8 * sub), b0 = *(const f32x4*)(Mu + 8 * sub + 4);
-  const f32x4 a1 = *(const f32x4*)(Mu + kD + 8 * sub), b1 = *(const f32x4*)(Mu + kD + 8 * sub + 4);
+  const float* m0p = Mu + (kSimple ? cs * kD : 0) + 8 * sub;
+  const f32x4 a0 = *(const f32x4*)m0p, b0 = *(const f32x4*)(m0p + 4);
   const float mu0[8] = {a0[0], a0[1], a0[2], a0[3], b0[0], b0[1], b0[2], b0[3]};
-  const float mu1[8] = {a1[0], a1[1], a1[2], a1[3], b1[0], b1[1], b1[2], b1[3]};
-  uint32_t vw[4][4];                                        // V^ words of the 4 keys
+  float mu1[8];
+  if (!kSimple) {
+    const f32x4 a1 = *(const f32x4*)(Mu + kD + 8 * sub), b1 = *(const f32x4*)(Mu + kD + 8 * sub + 4);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = 4 * (threadIdx.x >> 4) + i;
-    const bool second = s0 + key >= p.split;
+    for (int e = 0; e < 4; ++e) {
+      mu1[e] = a1[e];
+      mu1[4 + e] = b1[e];
+    }
+  }
+  const float sgk_s = cs ? p.sgk1 : p.sgk0, sgv_s = cs ? p.sgv1 : p.sgv0;
+  uint32_t vw[kKPT][4];                                     // V^ words of the thread's keys
+#pragma unroll
+  for (int i = 0; i < kKPT; ++i) {
+    const int key = kKPT * (threadIdx.x >> 4) + i;
     u32x4 ko, vo;
-    kv_unit_bf16<kVCheck>(r.kc[i], r.ks[i], r.vc[i], r.vs[i], second ? p.sgk1 : p.sgk0,
-                          second ? p.sgv1 : p.sgv0, second ? mu1 : mu0, ko, vo);
-    if (!p.mapped || s0 + key >= p.valid) {               // no key here: zeros, never NaN
-      ko = u32x4{0, 0, 0, 0};
-      vo = u32x4{0, 0, 0, 0};
+    if (kSimple) {
+      kv_unit_bf16<kVCheck>(r.kc[i], r.ks[i], r.vc[i], r.vs[i], sgk_s, sgv_s, mu0, ko, vo);
+    } else {
+      const bool second = s0 + key >= p.split;
+      kv_unit_bf16<kVCheck>(r.kc[i], r.ks[i], r.vc[i], r.vs[i], second ? p.sgk1 : p.sgk0,
+                            second ? p.sgv1 : p.sgv0, second ? mu1 : mu0, ko, vo);
+      if (!p.mapped || s0 + key >= p.valid) {               // no key: zeros, never NaN
+        ko = u32x4{0, 0, 0, 0};
+        vo = u32x4{0, 0, 0, 0};
+      }
     }
     *(u32x4*)(Ks + key * kKsRow + 8 * sub) = ko;
 #pragma unroll
@@ -132,13 +157,17 @@ __device__ __forceinline__ void decode_block(const PageInfo& p, int s0, const Bl
   }
   // V^T row 8 sub + c holds channel c of the 4 keys: bf16 of key i is the
   // low (c even) or high (c odd) half of vw[i][c / 2]
-  const int k0 = 4 * (threadIdx.x >> 4);
+  const int k0 = kKPT * (threadIdx.x >> 4);
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
     const uint32_t lo = __builtin_amdgcn_perm(vw[1][c >> 1], vw[0][c >> 1], sel);
-    const uint32_t hi = __builtin_amdgcn_perm(vw[3][c >> 1], vw[2][c >> 1], sel);
-    *(u32x2*)(Vt + (8 * sub + c) * kVtRow + k0) = u32x2{lo, hi};
+    if (kKPT == 4) {
+      const uint32_t hi = __builtin_amdgcn_perm(vw[kKPT - 1][c >> 1], vw[kKPT - 2][c >> 1], sel);
+      *(u32x2*)(Vt + (8 * sub + c) * kVtRow + k0) = u32x2{lo, hi};
+    } else {
+      *(uint32_t*)(Vt + (8 * sub + c) * kVtRow + k0) = lo;
+    }
   }
 }
 
@@ -171,7 +200,7 @@ size_t kv_attention_workspace_bytes(int64_t n_q, int64_t n_heads, int64_t n_keys
 // O values.
 // Two workgroups per CU (registers capped at 256 per lane), so one
 // workgroup's decode overlaps the other's MFMAs.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void kv_attention_kernel(KvGeom g, int64_t n_phys,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void kv_attention_kernel(KvGeom g, int64_t n_phys,
                                                            const int32_t* __restrict__ pages,
                                                            int n_pages, int last_tokens,
                                                            const uint16_t* __restrict__ q,
@@ -179,26 +208,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                            uint32_t q_sign,
                                                            uint16_t* __restrict__ out,
                                                            float* __restrict__ part, int n_split) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kKB * kKsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kD * kVtRow];
-  __shared__ __attribute__((aligned(16))) float Mu[2 * kD];    // K means: chunk c0, then c1
+  // LDS (kAttnLds bytes, dynamic): Q rows, K^ rows, V^T rows, K means of chunk c0 then c1
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  uint16_t* Qs = smem;
+  uint16_t* Ks = Qs + kQB * kKsRow;
+  uint16_t* Vt = Ks + kKB * kKsRow;
+  float* Mu = (float*)(Vt + kD * kVtRow);
   const int H = g.n_heads, P = g.page_tokens;
   const int h = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5;
   const int64_t qrow = (int64_t)blockIdx.x * kQB + wave * 32 + (lane & 31);
-  const int64_t qn = qrow < n_q ? qrow : n_q - 1;          // clamped rows are never stored
 
-  // Q as the B operand of S^T = K^ Q^T: step s covers channels 16 s .. 16 s + 15,
+  // The workgroup's 128 query rows go to LDS once (two threads per row, 64
+  // channels each); the first barrier of the block loop publishes them.  They
+  // are the B operand of S^T = K^ Q^T: step s covers channels 16 s .. 16 s + 15,
   // lane half `half` the 8 channels 16 s + 8 half ..
-  u32x4 qf[kD / 16];
   {
-    const uint16_t* qp = q + (qn * H + h) * kD + 8 * half;
+    const int row = tid >> 1;
+    const int64_t qr = (int64_t)blockIdx.x * kQB + row;
+    const uint16_t* qp = q + ((qr < n_q ? qr : n_q - 1) * H + h) * kD + 64 * (tid & 1);
+    uint16_t* qs = Qs + row * kKsRow + 64 * (tid & 1);
 #pragma unroll
-    for (int s = 0; s < kD / 16; ++s) {
-      qf[s] = *(const u32x4*)(qp + 16 * s);
+    for (int i = 0; i < 8; ++i) {
+      u32x4 v = *(const u32x4*)(qp + 8 * i);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qf[s][e] ^= q_sign;       // -q when the scale is negative
+      for (int e = 0; e < 4; ++e) v[e] ^= q_sign;           // -q when the scale is negative
+      *(u32x4*)(qs + 8 * i) = v;
     }
   }
   f32x16 o[kD / 32];
@@ -229,25 +265,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       fetch_block(g, pn, h, ((b + 1) % bpp) * kKB, rn);
     }
     if (pc.valid <= s0) continue;                           // whole block masked (uniform)
-    Mu[tid] = rc.mu;                       // safe: the previous decode's reads of Mu
+    if (tid < 2 * kD) Mu[tid] = rc.mu;     // safe: the previous decode's reads of Mu
     __syncthreads();                       // finished before the previous block's MFMAs
-    if (pc.vcheck)
-      decode_block<true>(pc, s0, rc, Mu, Ks, Vt);
-    else
-      decode_block<false>(pc, s0, rc, Mu, Ks, Vt);
+    {
+      const bool one_chunk = s0 + kKB <= pc.split || s0 >= pc.split;
+      const bool simple = pc.mapped && s0 + kKB <= pc.valid && one_chunk;
+      const int cs = s0 >= pc.split ? 1 : 0;
+      if (simple) {
+        if (pc.vcheck) decode_block<true, true>(pc, s0, cs, rc, Mu, Ks, Vt);
+        else decode_block<false, true>(pc, s0, cs, rc, Mu, Ks, Vt);
+      } else {
+        if (pc.vcheck) decode_block<true, false>(pc, s0, 0, rc, Mu, Ks, Vt);
+        else decode_block<false, false>(pc, s0, 0, rc, Mu, Ks, Vt);
+      }
+    }
     __syncthreads();
 
     // S^T tiles: keys 32 kt + (r / 4) * 8 + 4 half + r % 4 of this block, query lane % 32
+    // (the two key tiles' MFMA chains alternate, sharing each Q fragment)
     f32x16 st[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[kt][r] = 0.0f;
-      const uint16_t* kp = Ks + (32 * kt + (lane & 31)) * kKsRow + 8 * half;
+    {
+      const uint16_t* kp = Ks + (lane & 31) * kKsRow + 8 * half;
+      const uint16_t* qs = Qs + (wave * 32 + (lane & 31)) * kKsRow + 8 * half;
 #pragma unroll
-      for (int s = 0; s < kD / 16; ++s)
-        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*(const u32x4*)(kp + 16 * s)),
-                                                         as_bf16x8(qf[s]), st[kt], 0, 0, 0);
+      for (int s = 0; s < kD / 16; ++s) {
+        const bf16x8 qv = as_bf16x8(*(const u32x4*)(qs + 16 * s));
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+          st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              as_bf16x8(*(const u32x4*)(kp + 32 * kt * kKsRow + 16 * s)), qv, st[kt], 0, 0, 0);
+      }
     }
     // online softmax for this lane's query (keys split between lane and lane ^ 32),
     // in log2 units: t = S c with c = |scale| log2(e) >= 0, so the block max of t is
@@ -371,7 +422,12 @@ void launch_kv_attention(const KvGeom& g, const int32_t* logical_pages, int32_t 
   const uint32_t q_sign = softmax_scale < 0.0f ? 0x80008000u : 0u;
   const int n_split = attention_splits(n_q, g.n_heads, (int64_t)n_pages * g.page_tokens);
   const dim3 grid((unsigned)((n_q + kQB - 1) / kQB), (unsigned)g.n_heads, (unsigned)n_split);
-  hipLaunchKernelGGL(kv_attention_kernel, grid, dim3(256), 0, stream, g, g.n_phys_pages,
+  // dynamic LDS above the default 64 KB limit: raise it once (thread-safe static init)
+  static const bool configured =
+      hipFuncSetAttribute((const void*)kv_attention_kernel,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kAttnLds) == hipSuccess;
+  (void)configured;
+  hipLaunchKernelGGL(kv_attention_kernel, grid, dim3(kThreads), kAttnLds, stream, g, g.n_phys_pages,
                      logical_pages, n_pages, last_page_tokens, q, n_q, scale_log2e, q_sign, out,
                      (float*)workspace, n_split);
   if (n_split > 1) {

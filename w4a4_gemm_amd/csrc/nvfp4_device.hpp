@@ -31,8 +31,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return s;
 }
 
+// Two fp32 -> one dword of bf16 (lo in bits 15:0), both round to nearest even:
+// a vector conversion, which gfx950 does in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // ------------------------------------------------------------------ scales
