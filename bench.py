@@ -89,6 +89,17 @@ def next_op_table():
                              "compressed_bytes": 68 * 2 * 24 * 256 * (64 + 8),
                              "workload": (f"{ATTN_QUERIES} queries x 24 heads x 128 over a 68-page "
                                           "window (17408 keys), pages read as NVFP4; bf16 MFMA")},
+            # wgrad of FFN GEMM1, dW1 [14336 x 3072] = dY1^T X over 8192 tokens
+            "wgrad_quantize_t": {"bytes": 8192 * 14336 * (2 + NV_ELEM) + 4,
+                                 "workload": ("dY1 8192x14336 bf16 -> NVFP4 of dY1^T "
+                                              "(blocks along the tokens), tiled scales")},
+            "wgrad_gemm": {"flops": 2 * 14336 * 3072 * 8192,
+                           "workload": ("FFN GEMM1 wgrad M14336 N3072 K8192 (tokens), "
+                                        "both operands transposed-quantized, fp32 out")},
+            # host merge of three page ranges + one small launch writing the list
+            "window_pages": {"bytes": 68 * 4, "launch_bound": True,
+                             "workload": ("global sink 1024 + window 16384 of 65536 cached tokens "
+                                          "-> 68-page list on the device (launch-bound)")},
             # x read once, NVFP4 written, row stats written, modulation read once
             "adaln_quantize": {"bytes": m * k * (2 + NV_ELEM) + 4 + 8 * m + 2 * groups * k * 4,
                                "workload": ("FFN input 8192x3072 bf16: LayerNorm + adaLN modulate "
@@ -168,6 +179,17 @@ class Workload:
         self.ln_rpg = d["rows_per_group"]
         self.ln_q = nv.NVFP4Tensor(8192, 3072, nv.SCALES_TILED, device=dev)
         self.ln_stats = torch.empty((8192, 2), dtype=torch.float32, device=dev)
+        # next row: wgrad of FFN GEMM1 on transposed-quantized operands
+        gen = torch.Generator(device=dev).manual_seed(90)
+        self.wg_dy = (torch.randn((8192, 14336), generator=gen, device=dev) * 1e-3).to(
+            torch.bfloat16)
+        self.wg_dyq = nv.NVFP4Tensor(14336, 8192, nv.SCALES_TILED, device=dev)
+        self.wg_xq = nv.nvfp4_quantize_transposed(self.fx)
+        self.wg_out = torch.empty((14336, 3072), dtype=torch.float32, device=dev)
+        self.wg_ws = torch.empty(nv.nvfp4_workspace_bytes(nv.OP_QUANTIZE, 8192, 14336, 0),
+                                 dtype=torch.uint8, device=dev)
+        nv.nvfp4_quantize_transposed(self.wg_dy, out=self.wg_dyq, workspace=self.wg_ws)
+        self.win_pages = torch.empty(256, dtype=torch.int32, device=dev)
         self.ln_ws = torch.empty(nv.nvfp4_workspace_bytes(nv.OP_ADALN_QUANTIZE, 8192, 3072, 0),
                                  dtype=torch.uint8, device=dev)
         self._ops = self.ops()
@@ -207,6 +229,12 @@ class Workload:
         return [("kv_attention", lambda: nv.nvfp4_kv_attention(
                     self.lc, 0, self.window, self.attn_last, self.attn_q, 1.0 / 128 ** 0.5,
                     out=self.attn_out)),
+                ("wgrad_quantize_t", lambda: nv.nvfp4_quantize_transposed(
+                    self.wg_dy, out=self.wg_dyq, workspace=self.wg_ws)),
+                ("wgrad_gemm", lambda: nv.nvfp4_gemm_w4a4(self.wg_dyq, self.wg_xq,
+                                                          out=self.wg_out)),
+                ("window_pages", lambda: nv.nvfp4_kv_window_pages(
+                    65536, 256, 1024, 0, 0, 16384, pages=self.win_pages)),
                 ("adaln_quantize", lambda: nv.nvfp4_adaln_quantize(
                     self.ln_x, self.ln_shift, self.ln_scale, self.ln_rpg, 1e-6, out=self.ln_q,
                     row_stats=self.ln_stats, workspace=self.ln_ws))]
@@ -315,6 +343,36 @@ def cpu_baseline(ops):
     }
     step = sum(est.values())
     roof = sum(roofline_seconds(o) for o in ops.values())
+
+    # the rows measured beside the step: oracle per-unit times on small samples
+    from oracle import adaln as A
+    from oracle import training as T
+    from oracle import window as W
+    nxt_ops = next_op_table()
+    qa = F.bf16_bits_to_f64(synth.attn_queries(32, 24, 128, seed=50))
+    t = time.perf_counter()
+    KV.attention(pool, 0, list(range(kv_pages)), kv_tok - 256 * (kv_pages - 1), qa,
+                 1 / 128 ** 0.5)
+    t_attn = (time.perf_counter() - t) / (4 * 32 * kv_tok * 128 * 24)   # per FLOP
+    d = synth.adaln_input(m=256, k=3072)
+    xa = F.bf16_bits_to_f64(d["x"])
+    t = time.perf_counter()
+    A.adaln_quantize(xa, d["shift"][:1].astype(np.float64), d["scale"][:1].astype(np.float64),
+                     880, 1e-6)
+    t_ln = (time.perf_counter() - t) / xa.size
+    t = time.perf_counter()
+    T.quantize_transposed(x[:1024])
+    t_qt = (time.perf_counter() - t) / (1024 * 3072)
+    t = time.perf_counter()
+    W.window_pages(65536, 256, 1024, 0, 0, 16384)
+    t_win = time.perf_counter() - t
+    nxt = {
+        "kv_attention": t_attn * nxt_ops["kv_attention"]["flops"],
+        "wgrad_quantize_t": t_qt * 8192 * 14336,
+        "wgrad_gemm": t_gemm * nxt_ops["wgrad_gemm"]["flops"],
+        "adaln_quantize": t_ln * 8192 * 3072,
+        "window_pages": t_win,
+    }
     return {
         "value": 100.0 * roof / step,
         "unit": "% of MI355X roofline (whole step, extrapolated)",
@@ -324,8 +382,12 @@ def cpu_baseline(ops):
                    f"{g_rows}x3072x3072 exact GEMM, a {kv_tok}-token KV chunk write and "
                    f"{kv_pages} KV pages read; "
                    "per-unit times scaled to the full step; elementwise numpy is single-"
-                   "threaded, the GEMM's fp64 BLAS uses the listed threads"),
+                   "threaded, the GEMM's fp64 BLAS uses the listed threads; the rows beside "
+                   "the step: attention of 32 queries over those 28 pages, LayerNorm + adaLN + "
+                   "NVFP4 of 256 x 3072, transposed quantize of 1024 x 3072, the exact GEMM's "
+                   "per-FLOP time, and the whole window page list"),
         "step_seconds_estimate": step,
+        "next_ops_seconds_estimate": nxt,
     }
 
 
@@ -420,11 +482,14 @@ def main():
     nxt_rec = {}
     for n, o in next_op_table().items():
         t = nxt[n]
-        rec = {"ms": round(t * 1e3, 4), "roofline_frac": round(roofline_seconds(o) / t, 4),
-               "workload": o["workload"], "in_step": False}
-        if "flops" in o:
+        rec = {"ms": round(t * 1e3, 4), "workload": o["workload"], "in_step": False}
+        if o.get("launch_bound"):
+            rec["us_per_call"] = round(t * 1e6, 2)           # no meaningful roofline
+        elif "flops" in o:
+            rec["roofline_frac"] = round(roofline_seconds(o) / t, 4)
             rec["tflops"] = round(o["flops"] / t / 1e12, 2)
         else:
+            rec["roofline_frac"] = round(roofline_seconds(o) / t, 4)
             rec["gbps"] = round(o["bytes"] / t / 1e9, 1)
         nxt_rec[n] = rec
 
@@ -461,7 +526,12 @@ def main():
         "next_ops": nxt_rec,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(ops)
+        cb = cpu_baseline(ops)
+        for n, t_cpu in cb.pop("next_ops_seconds_estimate").items():
+            if n in nxt_rec:
+                nxt_rec[n]["oracle_seconds_estimate"] = t_cpu
+                nxt_rec[n]["gpu_speedup_vs_oracle"] = round(t_cpu / nxt[n], 1)
+        line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
 
 
