@@ -139,23 +139,6 @@ __device__ __forceinline__ void tile_of(int bid, int nbm, int nbn, int& tm, int&
   tn = in / rows;
 }
 
-// Decode blocks [b0, b0 + 2) of a slice (32 values) into an LDS row.
-__device__ __forceinline__ void decode_half(const Slice& sl, int half, uint16_t* __restrict__ row) {
-  const uint32_t cw[8] = {sl.c0[0], sl.c0[1], sl.c0[2], sl.c0[3],
-                          sl.c1[0], sl.c1[1], sl.c1[2], sl.c1[3]};
-  uint32_t sp[2];
-  scales4(sl.s, sp);
-#pragma unroll
-  for (int bb = 0; bb < 2; ++bb) {
-    const int b = 2 * half + bb;
-    uint32_t o[8];
-    decode8(cw[2 * b], sp[b >> 1], b & 1, o);
-    decode8(cw[2 * b + 1], sp[b >> 1], b & 1, o + 4);
-    *(u32x4*)(row + 16 * b) = u32x4{o[0], o[1], o[2], o[3]};
-    *(u32x4*)(row + 16 * b + 8) = u32x4{o[4], o[5], o[6], o[7]};
-  }
-}
-
 template <int TM, int TN, int WN>
 struct Frags {
   f16x8 a[TM], b[TN];

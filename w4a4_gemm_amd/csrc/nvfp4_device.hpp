@@ -326,13 +326,6 @@ __device__ __forceinline__ float pair_max(float v) {
   return fmaxf(v, __int_as_float(o));
 }
 
-// Lanes l, l+2, l+4, l+6 each hold one scale byte `sb`; lane l (l % 8 == 0)
-// receives them as one little-endian word.  Every lane must execute it.
-__device__ __forceinline__ uint32_t gather_scale_word(uint32_t sb) {
-  const uint32_t w2 = sb | ((uint32_t)__shfl_down((int)sb, 2, 64) << 8);
-  return w2 | ((uint32_t)__shfl_down((int)w2, 4, 64) << 16);
-}
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

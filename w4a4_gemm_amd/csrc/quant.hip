@@ -426,12 +426,6 @@ __device__ __forceinline__ float adaln_value(float x, float mu, float rstd, floa
   return n * gain + shift;
 }
 
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
 template <bool kBf16>
 __device__ __forceinline__ void chunk_values(const u32x4 w, float* v) {
 #pragma unroll
