@@ -22,7 +22,7 @@ namespace nvfp4 {
 
 namespace {
 
-constexpr int kStatsSlices = 8;           // token slices of the stats pass
+constexpr int kStatsSlices = 32;          // token slices of the stats pass
 constexpr int kStatsCols = 64;            // channels per stats workgroup (8 lanes x 8)
 constexpr int kFinalizeThreads = 256;
 
@@ -32,6 +32,7 @@ struct KvWorkspace {
   float* kmax;      // [slices][C]
   float* vamax;     // [stats workgroups]
   float* kamax;     // [finalize workgroups]
+  float* vamax_f;   // [finalize workgroups]: the stats partials of V folded per finalize workgroup
 };
 
 inline size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -48,7 +49,8 @@ KvWorkspace carve(void* ws, int64_t C, int n_stats_wg, int n_fin_wg) {
   w.vamax = (float*)p;
   p += round256(sizeof(float) * n_stats_wg);
   w.kamax = (float*)p;
-  (void)n_fin_wg;
+  p += round256(sizeof(float) * n_fin_wg);
+  w.vamax_f = (float*)p;
   return w;
 }
 
@@ -61,7 +63,7 @@ size_t kv_quantize_workspace_bytes(int64_t T, int64_t H, int64_t D) {
   (void)T;
   const int64_t C = H * D;
   return round256(sizeof(double) * kStatsSlices * C) + 2 * round256(sizeof(float) * kStatsSlices * C) +
-         round256(sizeof(float) * stats_wgs(C)) + round256(sizeof(float) * finalize_wgs(C));
+         round256(sizeof(float) * stats_wgs(C)) + 2 * round256(sizeof(float) * finalize_wgs(C));
 }
 
 // ------------------------------------------------------------------ 1. stats
@@ -156,8 +158,10 @@ __device__ __forceinline__ float mean_rn32(double S, int64_t T) {
   return f;
 }
 
+// Each workgroup also folds its share of the stats pass's V maxima, so the
+// quantize pass reads 2 x (finalize workgroups) partials for both tensor scales.
 __global__ __launch_bounds__(kFinalizeThreads) void kv_finalize_kernel(KvWorkspace ws, int64_t T,
-                                                                      int64_t C,
+                                                                      int64_t C, int n_stats_wg,
                                                                       float* __restrict__ mu_out) {
   const int64_t c = (int64_t)blockIdx.x * kFinalizeThreads + threadIdx.x;
   float amax = 0.0f;
@@ -173,14 +177,26 @@ __global__ __launch_bounds__(kFinalizeThreads) void kv_finalize_kernel(KvWorkspa
     mu_out[c] = mu;
     amax = fmaxf(hi - mu, mu - lo);              // each an RN32 of an exact difference
   }
+  float va = 0.0f;
+  for (int i = blockIdx.x * kFinalizeThreads + threadIdx.x; i < n_stats_wg;
+       i += gridDim.x * kFinalizeThreads)
+    va = fmaxf(va, ws.vamax[i]);
   amax = wave_max(amax);
-  __shared__ float red[kFinalizeThreads / 64];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  va = wave_max(va);
+  __shared__ float red[kFinalizeThreads / 64], redv[kFinalizeThreads / 64];
+  if ((threadIdx.x & 63) == 0) {
+    red[threadIdx.x >> 6] = amax;
+    redv[threadIdx.x >> 6] = va;
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
-    float m = red[0];
-    for (int i = 1; i < kFinalizeThreads / 64; ++i) m = fmaxf(m, red[i]);
+    float m = red[0], mv = redv[0];
+    for (int i = 1; i < kFinalizeThreads / 64; ++i) {
+      m = fmaxf(m, red[i]);
+      mv = fmaxf(mv, redv[i]);
+    }
     ws.kamax[blockIdx.x] = m;
+    ws.vamax_f[blockIdx.x] = mv;
   }
 }
 
@@ -198,7 +214,7 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(
     int64_t start_token, int32_t chunk_id, KvWorkspace ws, int n_stats_wg, int n_fin_wg,
     KvGeom g, int64_t n_phys, const float* __restrict__ mu_chunk) {
   const float s_gk = global_scale(max_of(ws.kamax, n_fin_wg));
-  const float s_gv = global_scale(max_of(ws.vamax, n_stats_wg));
+  const float s_gv = global_scale(max_of(ws.vamax_f, n_fin_wg));
   const TensorEnc tk = make_tensor_enc(s_gk), tv = make_tensor_enc(s_gv);
   const int H = g.n_heads, D = g.head_dim, P = g.page_tokens;
   const int gpr = (D + 63) / 64;                     // 64-value groups per (token, head)
@@ -535,6 +551,107 @@ __global__ __launch_bounds__(512) void kv_dequant_kernel(KvGeom g, int64_t n_phy
 
 // ------------------------------------------------------------------ launchers
 
+// Flat variant for head_dim dividing 512 (64, 128, 256): K and V are dense
+// [T][H][D], so lane u of the grid owns elements [8 u, 8 u + 8) -- one 16-byte
+// load per tensor, a wave reading 1 KB contiguous -- which is token
+// t = u / (H D / 8), head h, channels 8 j .. 8 j + 7 with j = u % (D / 8).  The
+// two lanes of a 16-value block exchange their maxima with one DPP swap (the
+// scheme of the activation quantize).  Whole waves stay in the loop (lanes past
+// the end take the last unit and store nothing) so the swap always has both
+// lanes; the loop strides over the grid.
+template <int kD, bool kPre>
+__device__ __forceinline__ void kv_flat_unit(const uint16_t* __restrict__ src,
+                                             const float* __restrict__ mu, int64_t u,
+                                             const TensorEnc& te, bool store, uint8_t* cp,
+                                             uint8_t* sp, int j) {
+  const u32x4 w = *(const u32x4*)(src + 8 * u);
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = bf16_lo(w[e]);
+    x[2 * e + 1] = bf16_hi(w[e]);
+  }
+  if (mu) {                                            // K' = RN32(K - mu)
+    const f32x4 m0 = *(const f32x4*)mu, m1 = *(const f32x4*)(mu + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = x[e] - m0[e];
+      x[4 + e] = x[4 + e] - m1[e];
+    }
+  }
+  float bm = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) bm = fmaxf(bm, __builtin_fabsf(x[e]));
+  bm = pair_max(bm);
+  const uint32_t sb = block_scale_byte(bm, te);
+  const BlockEnc enc = make_block_enc(sb, te);
+  if (kPre) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= 0x1p64f;
+  }
+  const uint32_t cw = encode8(x, enc, te);
+  if (store) {
+    *(uint32_t*)cp = cw;
+    if ((j & 1) == 0) *sp = (uint8_t)sb;
+  }
+}
+
+template <int kD>
+__global__ __launch_bounds__(256) void kv_quantize_flat_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t T,
+    int64_t start_token, int32_t chunk_id, KvWorkspace ws, int n_stats_wg, int n_fin_wg,
+    KvGeom g, int64_t n_phys, const float* __restrict__ mu_chunk) {
+  const float s_gk = global_scale(max_of(ws.kamax, n_fin_wg));
+  const float s_gv = global_scale(max_of(ws.vamax_f, n_fin_wg));
+  const TensorEnc tk = make_tensor_enc(s_gk), tv = make_tensor_enc(s_gv);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    g.k_gscale[chunk_id] = s_gk;
+    g.v_gscale[chunk_id] = s_gv;
+  }
+  constexpr int kLpr = kD / 8;                          // lanes per (token, head) row
+  const int H = g.n_heads, P = g.page_tokens;
+  const int64_t n = T * H * kLpr;
+  const int64_t codes_region = (int64_t)H * P * (kD / 2);
+  const int64_t scales_region = (int64_t)H * P * (kD / 16);
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  const int lane = threadIdx.x & 63;
+  for (int64_t base = (int64_t)blockIdx.x * 256 + (threadIdx.x - lane); base < n; base += stride) {
+    const int64_t u0 = base + lane;
+    const bool in = u0 < n;
+    const int64_t u = in ? u0 : n - 1;
+    const int64_t r = u / kLpr;                         // (token, head) row
+    const int j = (int)(u - r * kLpr);
+    const int64_t t = r / H;
+    const int h = (int)(r - t * H);
+    const int64_t pos = start_token + t;
+    const int64_t lp = pos / P;
+    const int slot = (int)(pos - lp * P);
+    // page -> chunk bookkeeping (one lane per touched page)
+    if (in && h == 0 && j == 0) {
+      if (t == 0) {
+        if (slot) g.page_chunk[2 * lp + 1] = slot;
+        else { g.page_chunk[2 * lp] = chunk_id; g.page_chunk[2 * lp + 1] = P; }
+      } else if (slot == 0) {
+        g.page_chunk[2 * lp] = chunk_id;
+        g.page_chunk[2 * lp + 1] = P;
+      }
+    }
+    const int64_t phys = g.page_table[lp];
+    const bool store = in && phys >= 0 && phys < n_phys;
+    uint8_t* page = g.pool + (store ? phys : 0) * g.page_bytes;
+    const int64_t row = (int64_t)h * P + slot;
+    uint8_t* kc = page + row * (kD / 2) + 4 * j;
+    uint8_t* ks = page + codes_region + row * (kD / 16) + (j >> 1);
+    uint8_t* vc = page + codes_region + scales_region + row * (kD / 2) + 4 * j;
+    uint8_t* vs = page + 2 * codes_region + scales_region + row * (kD / 16) + (j >> 1);
+    const float* mu = mu_chunk + (int64_t)h * kD + 8 * j;
+    if (tk.pre != 1.0f) kv_flat_unit<kD, true>(k, mu, u, tk, store, kc, ks, j);
+    else kv_flat_unit<kD, false>(k, mu, u, tk, store, kc, ks, j);
+    if (tv.pre != 1.0f) kv_flat_unit<kD, true>(v, nullptr, u, tv, store, vc, vs, j);
+    else kv_flat_unit<kD, false>(v, nullptr, u, tv, store, vc, vs, j);
+  }
+}
+
 void launch_kv_quantize(const KvGeom& g, int32_t chunk_id, const uint16_t* k, const uint16_t* v,
                         int64_t T, int64_t start_token, void* workspace, hipStream_t stream) {
   const int64_t C = (int64_t)g.n_heads * g.head_dim;
@@ -543,8 +660,22 @@ void launch_kv_quantize(const KvGeom& g, int32_t chunk_id, const uint16_t* k, co
   float* mu = g.k_mean + (int64_t)chunk_id * C;
   hipLaunchKernelGGL(kv_stats_kernel, dim3(nsw), dim3(256), 0, stream, k, v, T, C, ws);
   hipLaunchKernelGGL(kv_finalize_kernel, dim3(nfw), dim3(kFinalizeThreads), 0, stream, ws, T, C,
-                     mu);
-  const int gpr = (g.head_dim + 63) / 64;
+                     nsw, mu);
+  const int D = g.head_dim;
+  if (D == 64 || D == 128 || D == 256) {
+    const int64_t lanes = T * g.n_heads * (D / 8);
+    int64_t wgs = (lanes + 255) / 256;
+    wgs = wgs < 8192 ? wgs : 8192;                       // grid-stride beyond that
+    const auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(256), 0, stream, k, v, T, start_token,
+                         chunk_id, ws, nsw, nfw, g, g.n_phys_pages, (const float*)mu);
+    };
+    if (D == 64) go(kv_quantize_flat_kernel<64>);
+    else if (D == 128) go(kv_quantize_flat_kernel<128>);
+    else go(kv_quantize_flat_kernel<256>);
+    return;
+  }
+  const int gpr = (D + 63) / 64;
   const int tpw = 256 / gpr;
   const dim3 grid((unsigned)((T + tpw - 1) / tpw), (unsigned)g.n_heads);
   hipLaunchKernelGGL(kv_quantize_kernel, grid, dim3(256), 0, stream, k, v, T, start_token,
