@@ -105,22 +105,25 @@ def test_empty_and_single_row():
     _run(x, f32_tensor(x), shift, scale, 1, 1e-6, nv.SCALES_ROWMAJOR)
 
 
-def test_attn_proj_input_full_size_sampled_rows():
-    """DiT attention-projection input, 4096 x 3072 bf16, 880-row modulation groups,
-    tiled scales: every row's statistics, s_g, and the encoding of sampled rows
-    (the oracle's x' over the whole tensor gives the amax)."""
-    d = synth.adaln_input(m=4096, k=3072, seed=72)
+@pytest.mark.parametrize("m", [4096, 8192])
+def test_block_input_full_size_sampled_rows(m):
+    """DiT block inputs, m x 3072 bf16 (attention projection 4096 rows; FFN 8192
+    rows, the measured launch), 880-row modulation groups, tiled scales: every
+    row's statistics, s_g, and the encoding of sampled rows (the oracle's x' over
+    the whole tensor gives the amax)."""
+    d = synth.adaln_input(m=m, k=3072, seed=72)
     x, shift, scale, rpg = d["x"], d["shift"], d["scale"], d["rows_per_group"]
     t, stats = nv.nvfp4_adaln_quantize(bf16_tensor(x), f32_tensor(shift), f32_tensor(scale), rpg,
                                        1e-6, layout=nv.SCALES_TILED)
     got = to_oracle(t)
+    print(f"[adaln full size] {m} rows quantized", flush=True)
     x64 = F.bf16_bits_to_f64(x)
     mu, rstd, same = _check_stats(x64, stats.cpu().numpy(), 1e-6)
     assert same > 0.999
     xp = A.modulate(x64, mu, rstd, shift.astype(np.float64), scale.astype(np.float64), rpg)
     amax = float(np.max(np.abs(xp)))
-    rows = np.sort(np.random.default_rng(84).choice(4096, 96, replace=False))
-    rows = np.unique(np.concatenate([rows, [0, 879, 880, 4095]]))   # group edges
+    rows = np.sort(np.random.default_rng(84).choice(m, 96, replace=False))
+    rows = np.unique(np.concatenate([rows, [0, 879, 880, m - 1]]))   # group edges
     want = Q.quantize(xp[rows], amax=amax)
     assert got.s_g == want.s_g
     assert np.array_equal(got.scales[rows], want.scales)

@@ -129,3 +129,40 @@ def test_negative_and_zero_scale(scale):
     _write(gpu, ora, 0, kb, vb, 0)
     qb = synth.attn_queries(40, h, 128, seed=105)
     _check(gpu, ora, [0, 1, 2, 3, 4, 5], 330 - 5 * p, qb, scale, 6)
+
+
+@pytest.mark.slow
+def test_long_context_window_full_size_sampled():
+    """The measured launch: 880 queries x 24 heads over the 68-page window (4 sink
+    pages + the last 16384 tokens) of a 65536-token layer in shuffled pages, split
+    over workgroups and merged; sampled queries checked against the oracle."""
+    r = synth.LongContextKV(n_layers=1)
+    gpu = nv.KVCache(r.L, r.H, r.D, r.P, r.pages_per_layer, len(r.chunks), r.page_table,
+                     r.n_phys, device=dev())
+    ora = KV.KVPool(1, r.H, r.D, r.P, r.pages_per_layer, len(r.chunks),
+                    np.arange(r.pages_per_layer)[None, :], r.pages_per_layer)
+    window = r.window()
+    win_tokens = set()
+    for pg in window:
+        win_tokens.update((pg * r.P, pg * r.P + r.P - 1))
+    for c in range(len(r.chunks)):
+        start, kb, vb = r.chunk(0, c)
+        nv.nvfp4_kv_quantize(gpu, 0, c, bf16_tensor(kb), bf16_tensor(vb), start)
+        # the oracle needs only the chunks that hold window pages
+        if any(start <= t < start + len(kb) for t in win_tokens) or any(
+                start <= pg * r.P < start + len(kb) for pg in window):
+            ora.write_chunk(0, c, F.bf16_bits_to_f64(kb), F.bf16_bits_to_f64(vb), start)
+        print(f"[attention full size] chunk {c} written", flush=True)
+    assert nv.nvfp4_workspace_bytes(nv.OP_KV_ATTENTION, 880, r.H, len(window) * r.P) > 0
+    qb = synth.attn_queries(880, r.H, r.D, seed=50)
+    scale = 1 / math.sqrt(r.D)
+    lp = torch.tensor(window, dtype=torch.int32, device=dev())
+    out = nv.nvfp4_kv_attention(gpu, 0, lp, r.P, bf16_tensor(qb), scale)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    rows = np.unique(np.concatenate([[0, 127, 128, 879],
+                                     np.random.default_rng(106).choice(880, 20, replace=False)]))
+    ref, wabs = KV.attention(ora, 0, window, r.P, F.bf16_bits_to_f64(qb[rows]), scale,
+                             r.pages_per_layer)
+    bound = 2.0 ** -7 * wabs + 2.0 ** -8 * np.abs(ref) + 1e-30
+    assert float(np.max(np.abs(o[rows] - ref) / bound)) <= 1.0

@@ -105,3 +105,36 @@ def test_attn_proj_wgrad_full_size_sampled():
     rows = np.sort(np.random.default_rng(29).choice(3072, 24, replace=False))
     yref, aref = Q.gemm(ya, yb, rows=rows)
     _check(dw[torch.from_numpy(rows).to(dev())], yref, aref, False)
+
+
+@pytest.mark.slow
+def test_ffn_wgrad_full_size_sampled():
+    """The measured launch: wgrad of FFN GEMM1, dW1 [14336 x 3072] = dY1^T X over 8192
+    tokens, with the operands the benchmark uses (X the FFN input, dY1 ~ N(0, 1e-3)
+    from the device generator seeded 90).  Transposed operands: s_g and sampled
+    output rows bit-exact (the oracle takes the tensor amax of the whole input);
+    dW1 on sampled rows within the GEMM tolerance."""
+    f = synth.ffn_pair()
+    x = f["x"]
+    gen = torch.Generator(device=dev()).manual_seed(90)
+    dy_t = (torch.randn((8192, 14336), generator=gen, device=dev()) * 1e-3).to(torch.bfloat16)
+    a = nv.nvfp4_quantize_transposed(dy_t)
+    b = nv.nvfp4_quantize_transposed(bf16_tensor(x))
+    dw = nv.nvfp4_gemm_w4a4(a, b, dtype=torch.float32)
+    torch.cuda.synchronize()
+    print("[wgrad full size] device done", flush=True)
+    dy64 = dy_t.float().cpu().numpy().astype(np.float64)
+    got_a = to_oracle(a)
+    rows = np.unique(np.concatenate([[0, 14335], np.random.default_rng(30).choice(14336, 22,
+                                                                                  replace=False)]))
+    amax = float(np.max(np.abs(dy64)))
+    want_a = T.quantize_transposed(dy64[:, rows], amax=amax)
+    assert got_a.s_g == want_a.s_g
+    assert np.array_equal(got_a.packed[rows], want_a.packed)
+    assert np.array_equal(got_a.scales[rows], want_a.scales)
+    yb = T.quantize_transposed(F.bf16_bits_to_f64(x))
+    assert_same_nvfp4(to_oracle(b), yb)
+    print("[wgrad full size] operands checked", flush=True)
+    ya = Q.NVFP4(want_a.packed, want_a.scales, want_a.s_g)
+    yref, aref = Q.gemm(ya, yb)
+    _check(dw[torch.from_numpy(rows).to(dev())], yref, aref, False)
