@@ -7,13 +7,14 @@
 // the E2M1 codes in registers (the fused scale+quantize kernel the
 // ai-manual.ru article credits with a 20% saving).
 //
-// Layout of work (quantize and dequantize): a workgroup covers a tile of
-// 16 kTasks rows x 128 columns.  Lane l of wave w owns 8 consecutive values,
-// column chunk j = l % 16 of the tile, in rows 4 kTasks w + 4 t + l / 16 for
-// t < kTasks.  A wave's load instruction therefore reads 4 rows x 256
+// Layout of work (quantize and dequantize): with L = kLpr lanes per row and
+// R = 64 / L rows per wave instruction, a workgroup covers a tile of
+// 4 R kTasks rows x 8 L columns.  Lane l of wave w owns 8 consecutive values,
+// column chunk j = l % L of the tile, in rows R kTasks w + R t + l / L for
+// t < kTasks.  A wave's load instruction therefore reads R rows x 16 L
 // contiguous bytes (bf16), two neighbouring lanes form one 16-value block (the
-// even one stores its scale byte), a lane's 8 codes are one dword (16 lanes
-// store a row's 64 contiguous bytes), and the workgroup's rows lie inside one
+// even one stores its scale byte), a lane's 8 codes are one dword (L lanes
+// store 4 L contiguous bytes of a row), and the workgroup's rows lie inside one
 // 128-row band of the tiled scale layout.
 
 #include "launch.hpp"
@@ -25,9 +26,15 @@ namespace {
 #ifndef NVFP4_QUANT_TASKS
 #define NVFP4_QUANT_TASKS 4
 #endif
-constexpr int kTile = 128;                   // tile columns (and rows of the transposed tile)
+#ifndef NVFP4_QUANT_LPR
+#define NVFP4_QUANT_LPR 32
+#endif
+constexpr int kTile = 128;                   // tile of the transposed quantize
 constexpr int kTasks = NVFP4_QUANT_TASKS;    // rows per lane
-constexpr int kTileRows = 16 * kTasks;       // rows per workgroup: 4 waves x 4 rows x kTasks
+constexpr int kLpr = NVFP4_QUANT_LPR;        // lanes per row (8 values each)
+constexpr int kRpi = 64 / kLpr;              // rows per wave instruction
+constexpr int kTileCols = 8 * kLpr;          // columns per workgroup
+constexpr int kTileRows = 4 * kRpi * kTasks; // rows per workgroup: 4 waves x kRpi rows x kTasks
 constexpr int kAmaxUnroll = 8;     // 16-byte loads in flight per lane in the amax pass
 }  // namespace
 
@@ -158,7 +165,7 @@ __global__ __launch_bounds__(64) void publish_gscale_kernel(const float* __restr
 // encoding (a tensor-uniform choice, so the two variants are separate code).
 // `pro(t, v)` maps task t's 8 loaded values to the values that are quantized
 // (the identity for a plain quantize).
-template <int kN, bool kBf16, bool kTiled, bool kPre, typename Prologue>
+template <int kN, int kStep, bool kBf16, bool kTiled, bool kPre, typename Prologue>
 __device__ __forceinline__ void quantize_tasks(const Raw8* raw, const TensorEnc& te, int64_t r0,
                                                int64_t rows, bool cok, int j,
                                                uint8_t* __restrict__ cp,
@@ -180,7 +187,7 @@ __device__ __forceinline__ void quantize_tasks(const Raw8* raw, const TensorEnc&
       for (int e = 0; e < 8; ++e) v[e] *= 0x1p64f;
     }
     const uint32_t cw = encode8(v, enc, te);
-    if (cok && r0 + 4 * t < rows) {
+    if (cok && r0 + kStep * t < rows) {
       *(uint32_t*)(cp + t * c_step) = cw;
       if ((j & 1) == 0) sp[t * s_step] = (uint8_t)sb;
     }
@@ -193,9 +200,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     const float* __restrict__ amax, const float* __restrict__ partial,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gscale) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j = lane & 15;
-  const int64_t c0 = (int64_t)blockIdx.y * kTile + 8 * j;
-  const int64_t r0 = (int64_t)blockIdx.x * kTileRows + 4 * kTasks * wave + (lane >> 4);
+  const int j = lane & (kLpr - 1);
+  const int64_t c0 = (int64_t)blockIdx.y * kTileCols + 8 * j;
+  const int64_t r0 = (int64_t)blockIdx.x * kTileRows + kRpi * kTasks * wave + lane / kLpr;
   const bool cok = c0 < cols;
 
   // partial maxima first: in-order completion then lets task 0 start as soon
@@ -208,7 +215,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
   Raw8 raw[kTasks];
 #pragma unroll
   for (int t = 0; t < kTasks; ++t) {
-    const int64_t r = r0 + 4 * t;
+    const int64_t r = r0 + kRpi * t;
     raw[t] = load8<kBf16>(x, (r < rows ? r : rows - 1) * ld + cl);
   }
   float s_g = global_scale(amax ? *amax : reduce_partials(part));
@@ -222,14 +229,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(
   uint8_t* sp = scales + (kTiled ? ((r0 >> 7) * (cols / 64) + (kb >> 2)) * 512 +
                                        (r0 & 127) * 4 + (kb & 3)
                                  : r0 * (cols / 16) + kb);
-  const int64_t c_step = 4 * (cols / 2);
-  const int64_t s_step = kTiled ? 16 : 4 * (cols / 16);   // tiled: a 128-row band holds every task
+  const int64_t c_step = kRpi * (cols / 2);
+  const int64_t s_step = kTiled ? 4 * kRpi : kRpi * (cols / 16);   // tiled: a 128-row band holds every task
   const auto identity = [](int, float*) {};
   if (te.pre != 1.0f)
-    quantize_tasks<kTasks, kBf16, kTiled, true>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
+    quantize_tasks<kTasks, kRpi, kBf16, kTiled, true>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
                                         identity);
   else
-    quantize_tasks<kTasks, kBf16, kTiled, false>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
+    quantize_tasks<kTasks, kRpi, kBf16, kTiled, false>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
                                          identity);
 }
 
@@ -243,15 +250,15 @@ __global__ __launch_bounds__(256) void dequantize_kernel(
     const float* __restrict__ gscale, int64_t rows, int64_t cols, void* __restrict__ y,
     int64_t ld_y) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j = lane & 15;
-  const int64_t c0 = (int64_t)blockIdx.y * kTile + 8 * j;
-  const int64_t r0 = (int64_t)blockIdx.x * kTileRows + 4 * kTasks * wave + (lane >> 4);
+  const int j = lane & (kLpr - 1);
+  const int64_t c0 = (int64_t)blockIdx.y * kTileCols + 8 * j;
+  const int64_t r0 = (int64_t)blockIdx.x * kTileRows + kRpi * kTasks * wave + lane / kLpr;
   if (c0 >= cols) return;
 
   uint32_t cw[kTasks], sbyte[kTasks];
 #pragma unroll
   for (int t = 0; t < kTasks; ++t) {
-    const int64_t r = r0 + 4 * t;
+    const int64_t r = r0 + kRpi * t;
     cw[t] = 0;
     sbyte[t] = 0;
     if (r < rows) {
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(256) void dequantize_kernel(
 
 #pragma unroll
   for (int t = 0; t < kTasks; ++t) {
-    const int64_t r = r0 + 4 * t;
+    const int64_t r = r0 + kRpi * t;
     if (r >= rows) continue;
     const float s_b = e4m3_value(sbyte[t]);
     float out[8];
@@ -397,10 +404,10 @@ __global__ __launch_bounds__(256) void quantize_t_kernel(
   const int64_t s_step = kTiled ? 16 : 4 * (ocols / 16);
   const auto identity = [](int, float*) {};
   if (te.pre != 1.0f)
-    quantize_tasks<kTT, kBf16, kTiled, true>(raw, te, r0, orows, cok, j, cp, sp, c_step, s_step,
+    quantize_tasks<kTT, 4, kBf16, kTiled, true>(raw, te, r0, orows, cok, j, cp, sp, c_step, s_step,
                                         identity);
   else
-    quantize_tasks<kTT, kBf16, kTiled, false>(raw, te, r0, orows, cok, j, cp, sp, c_step, s_step,
+    quantize_tasks<kTT, 4, kBf16, kTiled, false>(raw, te, r0, orows, cok, j, cp, sp, c_step, s_step,
                                          identity);
 }
 
@@ -595,8 +602,8 @@ __global__ __launch_bounds__(256) void adaln_stats_kernel(
 }
 
 // Encode pass: the plain quantize tiling, with x' computed from the loaded x in
-// the prologue.  kTwoGroups: rows_per_group > 4 (kTasks - 1), so a lane's rows
-// r0 .. r0 + 4 (kTasks - 1) meet at most two modulation groups, whose vectors
+// the prologue.  kTwoGroups: rows_per_group > kRpi (kTasks - 1), so a lane's rows
+// r0 .. r0 + kRpi (kTasks - 1) meet at most two modulation groups, whose vectors
 // are loaded once; otherwise each task loads its own.
 template <bool kBf16, bool kTiled, bool kTwoGroups>
 __global__ __launch_bounds__(256) void adaln_quantize_kernel(
@@ -605,9 +612,9 @@ __global__ __launch_bounds__(256) void adaln_quantize_kernel(
     const float2* __restrict__ stats, const float* __restrict__ partial,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gscale) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j = lane & 15;
-  const int64_t c0 = (int64_t)blockIdx.y * kTile + 8 * j;
-  const int64_t r0 = (int64_t)blockIdx.x * kTileRows + 4 * kTasks * wave + (lane >> 4);
+  const int j = lane & (kLpr - 1);
+  const int64_t c0 = (int64_t)blockIdx.y * kTileCols + 8 * j;
+  const int64_t r0 = (int64_t)blockIdx.x * kTileRows + kRpi * kTasks * wave + lane / kLpr;
   const bool cok = c0 < cols;
 
   const Partials part = load_partials(partial);
@@ -616,12 +623,12 @@ __global__ __launch_bounds__(256) void adaln_quantize_kernel(
   float2 st[kTasks];
 #pragma unroll
   for (int t = 0; t < kTasks; ++t) {
-    const int64_t r = r0 + 4 * t;
+    const int64_t r = r0 + kRpi * t;
     const int64_t rc = r < rows ? r : rows - 1;
     raw[t] = load8<kBf16>(x, rc * ld + cl);
     st[t] = stats[rc];
   }
-  const int64_t ra = r0 < rows ? r0 : rows - 1;
+  const int64_t ra = r0 < rows ? r0 : rows - 1;   // the lane's rows: r0 .. r0 + kRpi (kTasks - 1)
   const int64_t ga = ra / rpg;
   const int64_t next = (ga + 1) * rpg;      // first row of the following group
   float sha[8], gna[8], shb[8], gnb[8];
@@ -638,7 +645,7 @@ __global__ __launch_bounds__(256) void adaln_quantize_kernel(
     }
   }
   const auto modulate = [&](int t, float* v) {
-    const int64_t r = r0 + 4 * t;
+    const int64_t r = r0 + kRpi * t;
     const int64_t rc = r < rows ? r : rows - 1;
     if (kTwoGroups) {
       const bool b = rc >= next;
@@ -665,13 +672,13 @@ __global__ __launch_bounds__(256) void adaln_quantize_kernel(
   uint8_t* sp = scales + (kTiled ? ((r0 >> 7) * (cols / 64) + (kb >> 2)) * 512 +
                                        (r0 & 127) * 4 + (kb & 3)
                                  : r0 * (cols / 16) + kb);
-  const int64_t c_step = 4 * (cols / 2);
-  const int64_t s_step = kTiled ? 16 : 4 * (cols / 16);
+  const int64_t c_step = kRpi * (cols / 2);
+  const int64_t s_step = kTiled ? 4 * kRpi : kRpi * (cols / 16);
   if (te.pre != 1.0f)
-    quantize_tasks<kTasks, kBf16, kTiled, true>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
+    quantize_tasks<kTasks, kRpi, kBf16, kTiled, true>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
                                         modulate);
   else
-    quantize_tasks<kTasks, kBf16, kTiled, false>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
+    quantize_tasks<kTasks, kRpi, kBf16, kTiled, false>(raw, te, r0, rows, cok, j, cp, sp, c_step, s_step,
                                          modulate);
 }
 
@@ -697,7 +704,7 @@ void launch_quantize(const void* x, bool x_bf16, int64_t rows, int64_t cols, int
                          x, rows, cols, ld, partial);
   }
   const dim3 grid((unsigned)((rows + kTileRows - 1) / kTileRows),
-                  (unsigned)((cols + kTile - 1) / kTile));
+                  (unsigned)((cols + kTileCols - 1) / kTileCols));
   if (rows == 0 || cols == 0) {
     hipLaunchKernelGGL(publish_gscale_kernel, dim3(1), dim3(64), 0, stream, amax, partial, gscale);
     return;
@@ -720,7 +727,7 @@ void launch_dequantize(const uint8_t* codes, const uint8_t* scales, bool tiled,
                        int64_t ld_y, hipStream_t stream) {
   if (rows == 0 || cols == 0) return;
   const dim3 grid((unsigned)((rows + kTileRows - 1) / kTileRows),
-                  (unsigned)((cols + kTile - 1) / kTile));
+                  (unsigned)((cols + kTileCols - 1) / kTileCols));
 #define NVFP4_DLAUNCH(T, B)                                                                  \
   hipLaunchKernelGGL((dequantize_kernel<T, B>), grid, dim3(256), 0, stream, codes, scales,   \
                      gscale, rows, cols, y, ld_y)
@@ -768,8 +775,8 @@ void launch_adaln_quantize(const void* x, bool x_bf16, int64_t rows, int64_t col
     return;
   }
   const dim3 grid((unsigned)((rows + kTileRows - 1) / kTileRows),
-                  (unsigned)((cols + kTile - 1) / kTile));
-  const bool two = rows_per_group > 4 * (kTasks - 1);
+                  (unsigned)((cols + kTileCols - 1) / kTileCols));
+  const bool two = rows_per_group > kRpi * (kTasks - 1);
   const auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, x, rows, cols, ld, shift, scale,
                        rows_per_group, stats, partial, codes, scales, gscale);
