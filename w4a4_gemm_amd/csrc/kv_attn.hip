@@ -181,10 +181,22 @@ int attention_splits(int64_t n_q, int64_t n_heads, int64_t n_keys) {
   const int64_t base = ((n_q + kQB - 1) / kQB) * n_heads;
   const int64_t blocks = (n_keys + kKB - 1) / kKB;
   if (base >= 512 || blocks < 16) return 1;
-  int64_t s = (1024 + base - 1) / base;
-  s = s < blocks / 8 ? s : blocks / 8;
-  s = s < 64 ? s : 64;
-  return s < 1 ? 1 : (int)s;
+  // Workgroups run two per CU (512 at once on 256 CUs).  Time ~ rounds of
+  // workgroups x blocks per workgroup, plus the merge, which reads every split's
+  // partial O (about 0.6 block-times per split here); each split keeps >= 8 blocks.
+  constexpr int64_t kSlots = 512;
+  const int64_t s_max = blocks / 8 < 64 ? blocks / 8 : 64;
+  int64_t best_s = 1;
+  double best = (double)blocks * ((base + kSlots - 1) / kSlots);
+  for (int64_t s = 2; s <= s_max; ++s) {
+    const double cost = (double)((base * s + kSlots - 1) / kSlots) * ((blocks + s - 1) / s) +
+                        0.6 * (double)s;
+    if (cost < best) {
+      best = cost;
+      best_s = s;
+    }
+  }
+  return (int)best_s;
 }
 
 size_t kv_attention_workspace_bytes(int64_t n_q, int64_t n_heads, int64_t n_keys) {
