@@ -15,6 +15,8 @@
 // blocks of a window): kv_dequant, one grid over (listed page, head, slot
 // tile), K^ = RN_bf16(q s_b s_gK + mu), V^ = RN_bf16(q s_b s_gV).
 
+#include <type_traits>
+
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -608,47 +610,72 @@ __global__ __launch_bounds__(256) void kv_quantize_flat_kernel(
     g.k_gscale[chunk_id] = s_gk;
     g.v_gscale[chunk_id] = s_gv;
   }
-  constexpr int kLpr = kD / 8;                          // lanes per (token, head) row
-  const int H = g.n_heads, P = g.page_tokens;
-  const int64_t n = T * H * kLpr;
-  const int64_t codes_region = (int64_t)H * P * (kD / 2);
-  const int64_t scales_region = (int64_t)H * P * (kD / 16);
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  const int lane = threadIdx.x & 63;
-  for (int64_t base = (int64_t)blockIdx.x * 256 + (threadIdx.x - lane); base < n; base += stride) {
-    const int64_t u0 = base + lane;
-    const bool in = u0 < n;
-    const int64_t u = in ? u0 : n - 1;
-    const int64_t r = u / kLpr;                         // (token, head) row
-    const int j = (int)(u - r * kLpr);
-    const int64_t t = r / H;
-    const int h = (int)(r - t * H);
-    const int64_t pos = start_token + t;
-    const int64_t lp = pos / P;
-    const int slot = (int)(pos - lp * P);
-    // page -> chunk bookkeeping (one lane per touched page)
-    if (in && h == 0 && j == 0) {
-      if (t == 0) {
-        if (slot) g.page_chunk[2 * lp + 1] = slot;
-        else { g.page_chunk[2 * lp] = chunk_id; g.page_chunk[2 * lp + 1] = P; }
-      } else if (slot == 0) {
-        g.page_chunk[2 * lp] = chunk_id;
-        g.page_chunk[2 * lp + 1] = P;
+  // 32-bit indices (the launcher checks T H D / 8 and start_token + T < 2^31).
+  // The grid stride is a whole number of rows, so a lane's (token, head) moves
+  // by a fixed step each iteration and its channel chunk j never changes.
+  constexpr uint32_t kLpr = kD / 8;                     // lanes per (token, head) row
+  const uint32_t H = g.n_heads, P = g.page_tokens;
+  const uint32_t n = (uint32_t)T * H * kLpr;
+  const uint32_t codes_region = H * P * (kD / 2);
+  const uint32_t scales_region = H * P * (kD / 16);
+  const uint32_t stride = gridDim.x * 256u;
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t u0 = blockIdx.x * 256u + threadIdx.x;
+  const uint32_t j = u0 % kLpr;
+  const uint32_t dr = stride / kLpr, dt = dr / H, dh = dr % H;
+  uint32_t r0 = u0 / kLpr;
+  uint32_t t = r0 / H, h = r0 % H;
+  const float* mu = mu_chunk + 8 * j;
+  // the encoders' pre-scaling is uniform per tensor: pick it outside the loop so
+  // the loop body has no branch between the K and V loads
+  const auto run = [&](auto pre_k, auto pre_v) {
+    constexpr bool kPk = decltype(pre_k)::value, kPv = decltype(pre_v)::value;
+    for (uint32_t base = blockIdx.x * 256u + (threadIdx.x - lane); base < n; base += stride) {
+      const uint32_t u = base + lane;
+      const bool in = u < n;
+      const uint32_t tc = in ? t : (uint32_t)T - 1;     // lanes past the end: valid addresses
+      const uint32_t uc = in ? u : n - 1;
+      const uint32_t pos = (uint32_t)start_token + tc;
+      const uint32_t lp = pos / P;
+      const uint32_t slot = pos - lp * P;
+      // page -> chunk bookkeeping (one lane per touched page)
+      if (in && h == 0 && j == 0) {
+        if (t == 0) {
+          if (slot) g.page_chunk[2 * lp + 1] = slot;
+          else { g.page_chunk[2 * lp] = chunk_id; g.page_chunk[2 * lp + 1] = P; }
+        } else if (slot == 0) {
+          g.page_chunk[2 * lp] = chunk_id;
+          g.page_chunk[2 * lp + 1] = P;
+        }
+      }
+      const int64_t phys = g.page_table[lp];
+      const bool store = in && phys >= 0 && phys < n_phys;
+      uint8_t* page = g.pool + (store ? phys : 0) * g.page_bytes;
+      const uint32_t row = h * P + slot;
+      uint8_t* kc = page + (row * (kD / 2) + 4 * j);
+      uint8_t* ks = page + (codes_region + row * (kD / 16) + (j >> 1));
+      uint8_t* vc = page + (codes_region + scales_region + row * (kD / 2) + 4 * j);
+      uint8_t* vs = page + (2 * codes_region + scales_region + row * (kD / 16) + (j >> 1));
+      kv_flat_unit<kD, kPk>(k, mu + h * kD, uc, tk, store, kc, ks, j);
+      kv_flat_unit<kD, kPv>(v, nullptr, uc, tv, store, vc, vs, j);
+      // next iteration's (token, head)
+      h += dh;
+      t += dt;
+      if (h >= H) {
+        h -= H;
+        t += 1;
       }
     }
-    const int64_t phys = g.page_table[lp];
-    const bool store = in && phys >= 0 && phys < n_phys;
-    uint8_t* page = g.pool + (store ? phys : 0) * g.page_bytes;
-    const int64_t row = (int64_t)h * P + slot;
-    uint8_t* kc = page + row * (kD / 2) + 4 * j;
-    uint8_t* ks = page + codes_region + row * (kD / 16) + (j >> 1);
-    uint8_t* vc = page + codes_region + scales_region + row * (kD / 2) + 4 * j;
-    uint8_t* vs = page + 2 * codes_region + scales_region + row * (kD / 16) + (j >> 1);
-    const float* mu = mu_chunk + (int64_t)h * kD + 8 * j;
-    if (tk.pre != 1.0f) kv_flat_unit<kD, true>(k, mu, u, tk, store, kc, ks, j);
-    else kv_flat_unit<kD, false>(k, mu, u, tk, store, kc, ks, j);
-    if (tv.pre != 1.0f) kv_flat_unit<kD, true>(v, nullptr, u, tv, store, vc, vs, j);
-    else kv_flat_unit<kD, false>(v, nullptr, u, tv, store, vc, vs, j);
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  const bool pk = tk.pre != 1.0f, pv = tv.pre != 1.0f;
+  if (pk) {
+    if (pv) run(yes{}, yes{});
+    else run(yes{}, no{});
+  } else {
+    if (pv) run(no{}, yes{});
+    else run(no{}, no{});
   }
 }
 
@@ -662,7 +689,10 @@ void launch_kv_quantize(const KvGeom& g, int32_t chunk_id, const uint16_t* k, co
   hipLaunchKernelGGL(kv_finalize_kernel, dim3(nfw), dim3(kFinalizeThreads), 0, stream, ws, T, C,
                      nsw, mu);
   const int D = g.head_dim;
-  if (D == 64 || D == 128 || D == 256) {
+  const bool small = T * g.n_heads * (D / 8) < (int64_t(1) << 31) &&
+                     start_token + T < (int64_t(1) << 31) &&
+                     g.page_bytes < (int64_t(1) << 32);
+  if ((D == 64 || D == 128 || D == 256) && small) {
     const int64_t lanes = T * g.n_heads * (D / 8);
     int64_t wgs = (lanes + 255) / 256;
     wgs = wgs < 8192 ? wgs : 8192;                       // grid-stride beyond that
