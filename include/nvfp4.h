@@ -126,7 +126,8 @@ int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, i
  *              16-byte aligned, ld_x * elem % 16 == 0
  *   amax       NULL, or a device float holding max|x| (X is then read once)
  *   out        (host struct) out->rows == cols, out->cols == rows
- *              (so rows % 16 == 0; tiled scales need cols % 128 and rows % 64)
+ *              (so rows % 16 == 0; tiled scales need cols % 128 and rows % 64;
+ *              cols <= 65535 * 128)
  *   workspace  nvfp4_workspace_bytes(NVFP4_OP_QUANTIZE, rows, cols, amax != NULL)
  * rows == 0 or cols == 0: only s_g (1.0, or from amax) is written.
  * Errors: EINVAL (nulls, dtype), ESHAPE (cols % 16, out dims, alignment,
@@ -244,9 +245,10 @@ int nvfp4_kv_quantize(const nvfp4_kv_cache_t* cache, int32_t layer, int32_t chun
  * window).  For each listed logical page, in list order:
  *   K^ = RN_bf16(q s_b s_gK + mu),  V^ = RN_bf16(q s_b s_gV)   (one rounding each)
  * using the chunk of every slot (page_chunk).
- *   logical_pages  device int32[n_pages], each in [0, max_pages)
+ *   logical_pages  device int32[n_pages]; an entry outside [0, max_pages), or
+ *                  one whose page-table entry is outside the pool, gives zero rows
  *   k_out, v_out   bf16 [n_pages * page_tokens][n_heads][head_dim], 16-byte aligned
- * Errors: EINVAL, ESHAPE. */
+ * Errors: EINVAL, ESHAPE (also ceil(page_tokens / 8) * n_pages >= 2^32). */
 int nvfp4_kv_dequant_blocks(const nvfp4_kv_cache_t* cache, int32_t layer,
                             const int32_t* logical_pages, int32_t n_pages, void* k_out,
                             void* v_out, void* stream);

@@ -226,3 +226,5 @@ def test_quantize_transposed_argument_errors():
     assert call(amax=258) == nv.ESHAPE
     assert call(w=None) == nv.EWORKSPACE
     assert call(o=T(16, 16, 64, 64, 128, nv.SCALES_TILED)) == nv.ESHAPE   # tiled needs 128 | out rows
+    wide = 65535 * 128 + 16                                   # beyond the grid's column tiles
+    assert call(cols=wide, ld=wide, o=T(16, 16, 64, wide, 128, nv.SCALES_ROWMAJOR)) == nv.ESHAPE

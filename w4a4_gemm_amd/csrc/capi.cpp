@@ -102,7 +102,7 @@ int nvfp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t rows, int6
   int st = check_tensor(out);
   if (st) return st;
   if (out->rows != cols || out->cols != rows) return NVFP4_ESHAPE;
-  if (cols % 16) return NVFP4_ESHAPE;
+  if (cols % 16 || cols > kMaxCols) return NVFP4_ESHAPE;    // grid.y: 128 input columns each
   const int64_t elem = x_dtype == NVFP4_BF16 ? 2 : 4;
   if (ld_x < cols || (ld_x * elem) % 16) return NVFP4_ESHAPE;
   if (rows > 0 && cols > 0 && !x) return NVFP4_EINVAL;
@@ -243,6 +243,8 @@ int nvfp4_kv_dequant_blocks(const nvfp4_kv_cache_t* cache, int32_t layer,
   if (st) return st;
   if (n_pages < 0) return NVFP4_EINVAL;
   if (n_pages == 0) return NVFP4_OK;
+  // one workgroup per 8-token tile of every listed page (a 1-D grid)
+  if ((int64_t)((g.page_tokens + 7) / 8) * n_pages >= (int64_t(1) << 32)) return NVFP4_ESHAPE;
   if (!logical_pages || !k_out || !v_out) return NVFP4_EINVAL;
   if (!aligned(k_out, 16) || !aligned(v_out, 16) || !aligned(logical_pages, 4))
     return NVFP4_ESHAPE;
