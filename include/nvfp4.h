@@ -179,13 +179,14 @@ int nvfp4_dequantize(const nvfp4_tensor_t* in, void* y, int32_t y_dtype, int64_t
  * (techwalker summary, section 四: every matrix multiplication in 4 bits).
  * Y = s_gx * s_gw * sum_k (q_x s_bx)(q_w s_bw): the block products are exact
  * and accumulate in fp32; the result is stored as y_dtype (fp32 or bf16, RNE).
- *   x, w    (host structs) K = x->cols = w->cols, K % 64 == 0; any scale layout
+ *   x, w    (host structs) K = x->cols = w->cols (any multiple of 16; K == 0
+ *           gives Y = 0); any scale layout
  *   y       M x N, row stride ld_y elements (ld_y >= N), 4-byte aligned rows
  *   y_amax  NULL, or a device float that the call max-folds max|Y as stored|
  *           into (atomic max; initialise it to 0 before the first GEMM whose
  *           amax it should hold).  Lets the next quantize read Y once.
  * M == 0 or N == 0 is a no-op.
- * Errors: EINVAL, ESHAPE (K mismatch, K % 64, ld_y). */
+ * Errors: EINVAL, ESHAPE (K mismatch, ld_y). */
 int nvfp4_gemm_w4a4(const nvfp4_tensor_t* x, const nvfp4_tensor_t* w, void* y, int32_t y_dtype,
                     int64_t ld_y, float* y_amax, void* stream);
 

@@ -72,12 +72,15 @@ def test_argument_errors_return_before_launch():
     # ld_x < cols
     assert lib.nvfp4_quantize(16, nv.BF16, 128, 64, 32, None, ctypes.byref(good), 256, 4096,
                               None) == nv.ESHAPE
-    # GEMM K mismatch and K % 64
+    # GEMM K mismatch, ld_y < N, K % 16 (any multiple of 16 is accepted: ragged K)
     w = T(16, 16, 64, 64, 128, nv.SCALES_ROWMAJOR)
     assert lib.nvfp4_gemm_w4a4(ctypes.byref(good), ctypes.byref(w), 16, nv.BF16, 64, None,
                                None) == nv.ESHAPE
     k48 = T(16, 16, 64, 64, 48, nv.SCALES_ROWMAJOR)
-    assert lib.nvfp4_gemm_w4a4(ctypes.byref(k48), ctypes.byref(k48), 16, nv.BF16, 64, None,
+    assert lib.nvfp4_gemm_w4a4(ctypes.byref(k48), ctypes.byref(k48), 16, nv.BF16, 32, None,
+                               None) == nv.ESHAPE
+    k40 = T(16, 16, 64, 64, 40, nv.SCALES_ROWMAJOR)
+    assert lib.nvfp4_gemm_w4a4(ctypes.byref(k40), ctypes.byref(k40), 16, nv.BF16, 64, None,
                                None) == nv.ESHAPE
     assert lib.nvfp4_gemm_w4a4(ctypes.byref(good), ctypes.byref(good), 16, 5, 128, None,
                                None) == nv.EINVAL

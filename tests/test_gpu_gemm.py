@@ -80,6 +80,31 @@ def test_ragged_shapes(m, n, k):
     assert Q.check_gemm_bf16(yb, y_ref, a_ref)[0]
 
 
+@pytest.mark.parametrize("m,n,k", [(96, 80, 16), (130, 70, 48), (257, 193, 80), (64, 300, 208),
+                                   (40, 24, 1040)])
+def test_ragged_k(m, n, k):
+    """K a multiple of 16 but not of 64: the last K step is partial (row-major
+    scales, rows on 8-byte code and 1-byte scale boundaries)."""
+    rng = np.random.default_rng(m + 5 * k)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    w = rng.standard_normal((n, k)).astype(np.float32)
+    xq, wq = _operands_from_f32(x, w)
+    y_ref, a_ref = Q.gemm(xq, wq)
+    y = _run(xq, wq, torch.float32, nv.SCALES_ROWMAJOR, nv.SCALES_ROWMAJOR)
+    assert Q.check_gemm_f32(y, y_ref, a_ref)[0]
+    yb, am = _run(xq, wq, torch.bfloat16, nv.SCALES_ROWMAJOR, nv.SCALES_ROWMAJOR, amax=True)
+    assert Q.check_gemm_bf16(yb, y_ref, a_ref)[0]
+    assert am == float(np.max(np.abs(yb)))
+
+
+def test_empty_k_gives_zeros():
+    """K == 0: the sum over k is empty, so Y = 0 (and max|Y| = 0)."""
+    xq = Q.quantize(np.zeros((70, 0)))
+    wq = Q.quantize(np.zeros((50, 0)))
+    y, am = _run(xq, wq, torch.bfloat16, nv.SCALES_ROWMAJOR, nv.SCALES_ROWMAJOR, amax=True)
+    assert y.shape == (70, 50) and not np.any(y) and am == 0.0
+
+
 def test_random_codes_and_all_scale_bytes():
     # arbitrary code bytes and every scale byte (incl. subnormal scales), odd s_g
     rng = np.random.default_rng(4)

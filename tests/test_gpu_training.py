@@ -89,6 +89,24 @@ def test_wgrad_and_dgrad_small(bf16_out):
     _check(dx, *T.dgrad(ya, yb), bf16_out)
 
 
+@pytest.mark.parametrize("bf16_out", [False, True])
+def test_wgrad_over_ragged_token_count(bf16_out):
+    """880 tokens (one latent frame): wgrad contracts over K = 880, a multiple of 16
+    but not of 64, so the transposed operands take row-major scales and the GEMM
+    ends with a partial K step."""
+    m, n, k = 880, 192, 320
+    x = synth.channel_outliers_bf16(m, k, seed=31, ch_seed=32)
+    dy = synth.weights_bf16(m, n, seed=33, std=1e-3)
+    x64, dy64 = F.bf16_bits_to_f64(x), F.bf16_bits_to_f64(dy)
+    a = nv.nvfp4_quantize_transposed(bf16_tensor(dy), layout=nv.SCALES_ROWMAJOR)
+    b = nv.nvfp4_quantize_transposed(bf16_tensor(x), layout=nv.SCALES_ROWMAJOR)
+    dw = nv.nvfp4_gemm_w4a4(a, b, dtype=torch.bfloat16 if bf16_out else torch.float32)
+    ya, yb = T.quantize_transposed(dy64), T.quantize_transposed(x64)
+    assert_same_nvfp4(to_oracle(a), ya)
+    assert_same_nvfp4(to_oracle(b), yb)
+    _check(dw, *T.wgrad(ya, yb), bf16_out)
+
+
 def test_attn_proj_wgrad_full_size_sampled():
     """wgrad of the attention projection: dW [3072 x 3072] = dY^T X over 4096 tokens;
     both transposed operands bit-exact in full, the product on sampled rows."""

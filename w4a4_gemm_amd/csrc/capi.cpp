@@ -168,7 +168,8 @@ int nvfp4_gemm_w4a4(const nvfp4_tensor_t* x, const nvfp4_tensor_t* w, void* y, i
   if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_EINVAL;
   if (x->cols != w->cols) return NVFP4_ESHAPE;
   const int64_t M = x->rows, N = w->rows, K = x->cols;
-  if (K % 64) return NVFP4_ESHAPE;
+  // K % 16 == 0 (check_tensor); K % 64 != 0 implies row-major scales (a tiled
+  // operand has cols % 64 == 0), which the GEMM's ragged-K path assumes
   if (ld_y < N) return NVFP4_ESHAPE;
   if (M > 0 && N > 0 && !y) return NVFP4_EINVAL;
   if (!aligned(y, 4) || (y_amax && !aligned(y_amax, 4))) return NVFP4_ESHAPE;

@@ -13,7 +13,8 @@
 // over every code and scale byte).
 //
 // Work decomposition
-//   * workgroup tile 256 x BN (BN = 256 or 192), K step 64; four waves in a
+//   * workgroup tile 256 x BN (BN = 256 or 192), K step 64 (a K that is not a
+//     multiple of 64 ends with a partial step, zero-filled); four waves in a
 //     2 x 2 grid, each owning a 128 x BN/2 block of 32 x 32 accumulators
 //     (v_mfma_f32_32x32x16_f16).
 //   * Each K step a thread fetches one 64-value slice of one X row and one W
@@ -28,6 +29,8 @@
 //   * Workgroups are remapped so that each of the 8 XCDs owns a contiguous run
 //     of tiles (better L2 reuse of shared X rows / W rows), grouped 8 tile
 //     rows at a time.
+
+#include <type_traits>
 
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
@@ -75,12 +78,34 @@ __device__ __forceinline__ RowSrc row_src(const Operand& o, int64_t r, int64_t K
   return rs;
 }
 
-__device__ __forceinline__ Slice fetch(const RowSrc& rs, int ks) {
+// Slice of K step ks.  kRag (K % 64 != 0, so row-major scales): rows start on
+// 8-byte code and 1-byte scale boundaries, so the slice is read in 8-byte code
+// pieces and single scale bytes, and of the last step only its vb valid blocks
+// are read (the rest are zero: zero codes with a zero scale contribute 0).
+template <bool kRag>
+__device__ __forceinline__ Slice fetch(const RowSrc& rs, int ks, int vb) {
   Slice sl;
   const uint8_t* cp = rs.codes + ks * 32;
-  sl.c0 = *(const u32x4*)cp;
-  sl.c1 = *(const u32x4*)(cp + 16);
-  sl.s = *(const uint32_t*)(rs.scales + (int64_t)ks * rs.sstride);
+  if (!kRag) {
+    sl.c0 = *(const u32x4*)cp;
+    sl.c1 = *(const u32x4*)(cp + 16);
+    sl.s = *(const uint32_t*)(rs.scales + (int64_t)ks * rs.sstride);
+    return sl;
+  }
+  const uint8_t* sp = rs.scales + (int64_t)ks * 4;
+  uint32_t c[8], s = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int bb = b < vb ? b : vb - 1;             // in-bounds address; value masked below
+    const u32x2 v = *(const u32x2*)(cp + 8 * bb);
+    const uint32_t sb = sp[bb];
+    c[2 * b] = b < vb ? v[0] : 0u;
+    c[2 * b + 1] = b < vb ? v[1] : 0u;
+    s |= (b < vb ? sb : 0u) << (8 * b);
+  }
+  sl.c0 = u32x4{c[0], c[1], c[2], c[3]};
+  sl.c1 = u32x4{c[4], c[5], c[6], c[7]};
+  sl.s = s;
   return sl;
 }
 
@@ -265,7 +290,7 @@ __device__ __forceinline__ void store_tile(const f32x16& a, float scale, void* y
 
 }  // namespace
 
-template <int BN, bool kOutBf16>
+template <int BN, bool kOutBf16, bool kRag>
 __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_kernel(
     Operand xa, Operand wb, const float* __restrict__ xg, const float* __restrict__ wg, int M,
     int N, int64_t K, void* __restrict__ y, int64_t ld_y, float* __restrict__ y_amax, int nbm,
@@ -279,7 +304,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_kernel(
   tile_of(blockIdx.x, nbm, nbn, tm, tn);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nk = (int)(K / kBK);
+  const int nk = (int)((K + kBK - 1) / kBK);      // K steps; the last is partial when kRag
+  const int kbt = (int)(K / 16);                  // 16-value blocks along K
+  auto vb = [&](int ks) { return kbt - 4 * ks < 4 ? kbt - 4 * ks : 4; };
 
   // Loader rows, clamped into range (results of clamped rows are never
   // stored).  With BN < 256 the spare threads load a valid W row and write it
@@ -300,27 +327,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_kernel(
   // loads of step s+2.  The decode (VALU + LDS stores) and the MFMAs of a step
   // are independent, so they form one basic block that the scheduler
   // interleaves; one barrier per step.
-  {
-    const Slice a0 = fetch(ra, 0), b0 = fetch(rb, 0);
-    decode_to_lds(a0, lds + tid * kLdsRow);
-    decode_to_lds(b0, lds + (kBM + tid) * kLdsRow);
-  }
-  Slice ca = fetch(ra, nk > 1 ? 1 : 0), cb = fetch(rb, nk > 1 ? 1 : 0);
-  __syncthreads();
-  Frags<TM, TN, WN> f0, f1;
-  load_frags(f0, lds, lds + kBM * kLdsRow, 0, lane, wm, wn);
-
-  for (int s = 0; s < nk; ++s) {
-    const int cur = s & 1;
-    const int s2 = s + 2 < nk ? s + 2 : nk - 1;
-    const Slice na = fetch(ra, s2), nb = fetch(rb, s2);
-    const uint16_t* As = lds + cur * kStage;
-    uint16_t* An = lds + (cur ^ 1) * kStage;
-    gemm_step<TM, TN, WN>(acc, f0, f1, As, As + kBM * kLdsRow, An, ca, cb, tid, lane, wm, wn);
+  if (nk > 0) {             // K == 0: no step, Y = 0
+    {
+      const Slice a0 = fetch<kRag>(ra, 0, vb(0)), b0 = fetch<kRag>(rb, 0, vb(0));
+      decode_to_lds(a0, lds + tid * kLdsRow);
+      decode_to_lds(b0, lds + (kBM + tid) * kLdsRow);
+    }
+    const int s1 = nk > 1 ? 1 : 0;
+    Slice ca = fetch<kRag>(ra, s1, vb(s1)), cb = fetch<kRag>(rb, s1, vb(s1));
     __syncthreads();
-    load_frags(f0, An, An + kBM * kLdsRow, 0, lane, wm, wn);   // sub-step 0 of the next step
-    ca = na;
-    cb = nb;
+    Frags<TM, TN, WN> f0, f1;
+    load_frags(f0, lds, lds + kBM * kLdsRow, 0, lane, wm, wn);
+
+    for (int s = 0; s < nk; ++s) {
+      const int cur = s & 1;
+      const int s2 = s + 2 < nk ? s + 2 : nk - 1;
+      const Slice na = fetch<kRag>(ra, s2, vb(s2)), nb = fetch<kRag>(rb, s2, vb(s2));
+      const uint16_t* As = lds + cur * kStage;
+      uint16_t* An = lds + (cur ^ 1) * kStage;
+      gemm_step<TM, TN, WN>(acc, f0, f1, As, As + kBM * kLdsRow, An, ca, cb, tid, lane, wm, wn);
+      __syncthreads();
+      load_frags(f0, An, An + kBM * kLdsRow, 0, lane, wm, wn);   // sub-step 0 of the next step
+      ca = na;
+      cb = nb;
+    }
   }
 
   // epilogue: Y = acc * (s_gx s_gw), rounded once to the output type
@@ -340,13 +370,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_kernel(
   }
 }
 
-template <int BN, bool kOutBf16>
+template <int BN, bool kOutBf16, bool kRag>
 static void launch_bn(const Operand& xa, const Operand& wb, const float* xg, const float* wg,
                       int64_t M, int64_t N, int64_t K, void* y, int64_t ld_y, float* y_amax,
                       hipStream_t stream) {
   const int nbm = (int)((M + kBM - 1) / kBM), nbn = (int)((N + BN - 1) / BN);
   const size_t lds = 2 * (size_t)(2 * kBM) * kLdsRow * sizeof(uint16_t);
-  auto kern = gemm_w4a4_kernel<BN, kOutBf16>;
+  auto kern = gemm_w4a4_kernel<BN, kOutBf16, kRag>;
   // raise the dynamic-LDS limit once per instantiation (thread-safe static init)
   static const bool configured =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -367,13 +397,17 @@ void launch_gemm(const uint8_t* xc, const uint8_t* xs, bool x_tiled, const float
   const int64_t t256 = nbm * ((N + 255) / 256), t192 = nbm * ((N + 191) / 192);
   auto waves = [](int64_t t) { return (t + 255) / 256; };
   const bool use192 = waves(t192) * 192 < waves(t256) * 256;
-  if (use192) {
-    if (y_bf16) launch_bn<192, true>(xa, wb, xg, wg, M, N, K, y, ld_y, y_amax, stream);
-    else launch_bn<192, false>(xa, wb, xg, wg, M, N, K, y, ld_y, y_amax, stream);
-  } else {
-    if (y_bf16) launch_bn<256, true>(xa, wb, xg, wg, M, N, K, y, ld_y, y_amax, stream);
-    else launch_bn<256, false>(xa, wb, xg, wg, M, N, K, y, ld_y, y_amax, stream);
-  }
+  const bool rag = K % kBK != 0;
+  auto go = [&](auto bn, auto out_bf16, auto ragged) {
+    launch_bn<decltype(bn)::value, decltype(out_bf16)::value, decltype(ragged)::value>(
+        xa, wb, xg, wg, M, N, K, y, ld_y, y_amax, stream);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  auto go_rag = [&](auto bn, auto out_bf16) { rag ? go(bn, out_bf16, T{}) : go(bn, out_bf16, F{}); };
+  auto go_out = [&](auto bn) { y_bf16 ? go_rag(bn, T{}) : go_rag(bn, F{}); };
+  if (use192) go_out(std::integral_constant<int, 192>{});
+  else go_out(std::integral_constant<int, 256>{});
 }
 
 }  // namespace nvfp4
