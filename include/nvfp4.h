@@ -67,7 +67,7 @@ typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype_t;
 typedef enum { NVFP4_SCALES_ROWMAJOR = 0, NVFP4_SCALES_TILED = 1 } nvfp4_scale_layout_t;
 
 /* An NVFP4 tensor [rows x cols] (cols % 16 == 0, cols <= 65535 * 128,
- * rows <= 2^37; larger sizes give ESHAPE).  The struct itself is a host
+ * rows <= 2^28; larger sizes give ESHAPE).  The struct itself is a host
  * object; its pointers are device pointers. */
 typedef struct {
   uint8_t* codes;        /* rows * cols / 2 bytes                               */
@@ -235,8 +235,8 @@ int64_t nvfp4_kv_page_bytes(int32_t n_heads, int32_t head_dim, int32_t page_toke
  * the touched pages must be valid physical pages.  The mean is accumulated in
  * fp64 in a fixed order; it is exact while the partial sums of a channel stay
  * within fp64's 53 bits (true for bf16 data of moderate dynamic range).
- * Errors: EINVAL, ESHAPE (T < page_tokens unless it is chunk 0, head_dim,
- * token range past max_pages, chunk_id >= max_chunks), EWORKSPACE. */
+ * Errors: EINVAL, ESHAPE (T < page_tokens unless it is chunk 0, T >= 2^30,
+ * head_dim, token range past max_pages, chunk_id >= max_chunks), EWORKSPACE. */
 int nvfp4_kv_quantize(const nvfp4_kv_cache_t* cache, int32_t layer, int32_t chunk_id,
                       const void* k_bf16, const void* v_bf16, int64_t T, int64_t start_token,
                       void* workspace, size_t ws_bytes, void* stream);

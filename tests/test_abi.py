@@ -90,6 +90,9 @@ def test_argument_errors_return_before_launch():
                                None) == nv.OK
     # dequantize: bad out dtype
     assert lib.nvfp4_dequantize(ctypes.byref(good), 16, 9, 64, None) == nv.EINVAL
+    # more rows than one grid dimension can cover (2^28 is the limit)
+    huge = T(16, 16, 64, (1 << 28) + 32, 16, nv.SCALES_ROWMAJOR)
+    assert lib.nvfp4_dequantize(ctypes.byref(huge), 16, nv.F32, 16, None) == nv.ESHAPE
 
 
 def test_kv_argument_errors():

@@ -24,9 +24,12 @@ inline int finish() {
 
 inline hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
-// quantize/dequantize grids: one workgroup per 128 x 128 tile, columns on grid.y
+// Tensor size limits from the launch grids: columns go on grid.y (at most
+// 65535 workgroups of 128 input columns in the transposed quantize), rows on
+// grid.x, where quantize/dequantize/adaLN run one 256-thread workgroup per 32
+// rows and one grid dimension holds fewer than 2^32 work-items.
 constexpr int64_t kMaxCols = int64_t(65535) * 128;
-constexpr int64_t kMaxRows = int64_t(1) << 37;
+constexpr int64_t kMaxRows = int64_t(1) << 28;
 
 int check_tensor(const nvfp4_tensor_t* t) {
   if (!t) return NVFP4_EINVAL;
@@ -227,7 +230,8 @@ int nvfp4_kv_quantize(const nvfp4_kv_cache_t* cache, int32_t layer, int32_t chun
   if (T < cache->page_tokens && chunk_id != 0) return NVFP4_ESHAPE;
   if ((start_token + T + cache->page_tokens - 1) / cache->page_tokens > cache->max_pages)
     return NVFP4_ESHAPE;
-  if (T >= (int64_t(1) << 31)) return NVFP4_ESHAPE;
+  // the general quantize kernel runs one workgroup per >= 64 tokens on grid.x
+  if (T >= (int64_t(1) << 30)) return NVFP4_ESHAPE;
   const size_t need = nvfp4::kv_quantize_workspace_bytes(T, cache->n_heads, cache->head_dim);
   if (!workspace || ws_bytes < need || !aligned(workspace, 256)) return NVFP4_EWORKSPACE;
   (void)hipGetLastError();
