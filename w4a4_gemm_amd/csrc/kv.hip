@@ -71,7 +71,9 @@ size_t kv_quantize_workspace_bytes(int64_t T, int64_t H, int64_t D) {
 // ------------------------------------------------------------------ 1. stats
 
 // Workgroup (colgroup, slice): 8 lanes cover 64 channels (8 each, one 16-byte
-// load), 32 token lanes stride over the slice's tokens.
+// load), 32 token lanes stride over the slice's tokens, kStatsUnroll tokens at
+// a time.
+constexpr int kStatsUnroll = 8;
 __global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ v,
                                                        int64_t T, int64_t C, KvWorkspace ws) {
@@ -86,21 +88,33 @@ __global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t* __restric
 #pragma unroll
   for (int j = 0; j < 8; ++j) { s[j] = 0.0; mn[j] = __builtin_inff(); mx[j] = -__builtin_inff(); }
   const bool active = c0 < C;
-  if (active) {
-    for (int64_t t = t0 + tl; t < t1; t += 32) {
-      const u32x4 kw = *(const u32x4*)(k + t * C + c0);
-      const u32x4 vw = *(const u32x4*)(v + t * C + c0);
+  if (active && t0 < t1) {
+    // kStatsUnroll tokens' loads in flight per lane; a token past the slice
+    // loads the slice's last row again (min, max and amax unchanged) and is
+    // left out of the sum
+    for (int64_t tb = t0 + tl; tb < t1; tb += 32 * kStatsUnroll) {
+      u32x4 kw[kStatsUnroll], vw[kStatsUnroll];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a = bf16_lo(kw[j]), b = bf16_hi(kw[j]);
-        s[2 * j] += (double)a;
-        s[2 * j + 1] += (double)b;
-        mn[2 * j] = fminf(mn[2 * j], a);
-        mn[2 * j + 1] = fminf(mn[2 * j + 1], b);
-        mx[2 * j] = fmaxf(mx[2 * j], a);
-        mx[2 * j + 1] = fmaxf(mx[2 * j + 1], b);
-        const uint32_t av = vw[j] & 0x7FFF7FFFu;
-        va = max(va, max(av & 0xFFFFu, av >> 16));
+      for (int u = 0; u < kStatsUnroll; ++u) {
+        const int64_t t = tb + 32 * u < t1 ? tb + 32 * u : t1 - 1;
+        kw[u] = *(const u32x4*)(k + t * C + c0);
+        vw[u] = *(const u32x4*)(v + t * C + c0);
+      }
+#pragma unroll
+      for (int u = 0; u < kStatsUnroll; ++u) {
+        const bool in = tb + 32 * u < t1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float a = bf16_lo(kw[u][j]), b = bf16_hi(kw[u][j]);
+          s[2 * j] += in ? (double)a : 0.0;
+          s[2 * j + 1] += in ? (double)b : 0.0;
+          mn[2 * j] = fminf(mn[2 * j], a);
+          mn[2 * j + 1] = fminf(mn[2 * j + 1], b);
+          mx[2 * j] = fmaxf(mx[2 * j], a);
+          mx[2 * j + 1] = fmaxf(mx[2 * j + 1], b);
+          const uint32_t av = vw[u][j] & 0x7FFF7FFFu;
+          va = max(va, max(av & 0xFFFFu, av >> 16));
+        }
       }
     }
   }
