@@ -21,7 +21,10 @@ and the 2.5 PFLOP/s dense fp16 MFMA peak for the GEMMs, which run on the
 fp16 MFMA) divided by the
 measured step time.  Per-op rates (GB/s, TFLOP/s) and fractions are reported
 alongside, plus the roofline of the dominant kernel (the FFN GEMM1 launch)
-and the CPU oracle's rate on a bounded sample of the same work.
+and the CPU oracle's rate on a bounded sample of the same work.  Per-op times
+are in-step (inputs cold in the Infinity Cache: the step streams GBs between
+reuses); hot_ms is the same op repeated back to back, and copy_frac is a
+bandwidth op's in-step rate over a measured 1 GiB device copy (hbm_copy_gbps).
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --only OP [--reps N]     one op of the step, N times (profiling)
@@ -278,6 +281,19 @@ def run_gpu(steps, warmup):
         for (n, a), (_, b) in zip(evs[:-1], evs[1:]):
             acc[n] += a.elapsed_time(b) * 1e-3
     per_op = {n: acc[n] / steps for n in names}
+    # each op of the step repeated back to back: its inputs stay in the 256 MB
+    # Infinity Cache where they fit (the step streams GBs between reuses)
+    hot = {}
+    for n, fn in wl._ops:
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        hot[n] = a.elapsed_time(b) * 1e-3 / steps
     nxt = {}
     for n, fn in wl.next_ops():
         fn()
@@ -289,7 +305,26 @@ def run_gpu(steps, warmup):
         b.record()
         torch.cuda.synchronize()
         nxt[n] = a.elapsed_time(b) * 1e-3 / steps
-    return wall, per_op, nxt
+    return wall, per_op, hot, nxt, copy_bytes_per_second(torch)
+
+
+def copy_bytes_per_second(torch, nbytes=1 << 30, reps=5):
+    """A plain 1 GiB device copy (read + write bytes per second): the
+    measured reference for the bandwidth-bound ops."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    del src, dst
+    return 2 * nbytes / sorted(ts)[reps // 2]
 
 
 # ------------------------------------------------------------------ CPU oracle baseline
@@ -464,17 +499,19 @@ def main():
         return
 
     ops = op_table()
-    wall, per_op, nxt = run_gpu(args.steps, args.warmup)
+    wall, per_op, hot, nxt, copy_bps = run_gpu(args.steps, args.warmup)
     roof = sum(roofline_seconds(o) for o in ops.values())
 
     per = {}
     for n, o in ops.items():
         s = per_op[n]
-        rec = {"ms": round(s * 1e3, 4), "roofline_frac": round(roofline_seconds(o) / s, 4)}
+        rec = {"ms": round(s * 1e3, 4), "roofline_frac": round(roofline_seconds(o) / s, 4),
+               "hot_ms": round(hot[n] * 1e3, 4)}
         if "flops" in o:
             rec["tflops"] = round(o["flops"] / s / 1e12, 2)
         else:
             rec["gbps"] = round(o["bytes"] / s / 1e9, 1)
+            rec["copy_frac"] = round(o["bytes"] / s / copy_bps, 4)
         if "compressed_bytes" in o:
             rec["gbps_compressed_read"] = round(o["compressed_bytes"] / s / 1e9, 1)
         per[n] = rec
@@ -522,6 +559,7 @@ def main():
             "frac": round(ops["ffn_gemm1"]["flops"] / g1 / MFMA_F16_FLOPS, 4),
             "traffic": measured_traffic(),
         },
+        "hbm_copy_gbps": round(copy_bps / 1e9, 1),
         "per_op": per,
         "next_ops": nxt_rec,
     }
