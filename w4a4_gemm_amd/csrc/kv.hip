@@ -227,7 +227,7 @@ __device__ __forceinline__ float max_of(const float* p, int n) {
 // Thread -> (token, 64-channel group of head_dim) for one head (blockIdx.y).
 __global__ __launch_bounds__(256) void kv_quantize_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t T,
-    int64_t start_token, int32_t chunk_id, KvWorkspace ws, int n_stats_wg, int n_fin_wg,
+    int64_t start_token, int32_t chunk_id, KvWorkspace ws, int n_fin_wg,
     KvGeom g, int64_t n_phys, const float* __restrict__ mu_chunk) {
   const float s_gk = global_scale(max_of(ws.kamax, n_fin_wg));
   const float s_gv = global_scale(max_of(ws.vamax_f, n_fin_wg));
@@ -615,7 +615,7 @@ __device__ __forceinline__ void kv_flat_unit(const uint16_t* __restrict__ src,
 template <int kD>
 __global__ __launch_bounds__(256) void kv_quantize_flat_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t T,
-    int64_t start_token, int32_t chunk_id, KvWorkspace ws, int n_stats_wg, int n_fin_wg,
+    int64_t start_token, int32_t chunk_id, KvWorkspace ws, int n_fin_wg,
     KvGeom g, int64_t n_phys, const float* __restrict__ mu_chunk) {
   const float s_gk = global_scale(max_of(ws.kamax, n_fin_wg));
   const float s_gv = global_scale(max_of(ws.vamax_f, n_fin_wg));
@@ -712,7 +712,7 @@ void launch_kv_quantize(const KvGeom& g, int32_t chunk_id, const uint16_t* k, co
     wgs = wgs < 8192 ? wgs : 8192;                       // grid-stride beyond that
     const auto go = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(256), 0, stream, k, v, T, start_token,
-                         chunk_id, ws, nsw, nfw, g, g.n_phys_pages, (const float*)mu);
+                         chunk_id, ws, nfw, g, g.n_phys_pages, (const float*)mu);
     };
     if (D == 64) go(kv_quantize_flat_kernel<64>);
     else if (D == 128) go(kv_quantize_flat_kernel<128>);
@@ -723,7 +723,7 @@ void launch_kv_quantize(const KvGeom& g, int32_t chunk_id, const uint16_t* k, co
   const int tpw = 256 / gpr;
   const dim3 grid((unsigned)((T + tpw - 1) / tpw), (unsigned)g.n_heads);
   hipLaunchKernelGGL(kv_quantize_kernel, grid, dim3(256), 0, stream, k, v, T, start_token,
-                     chunk_id, ws, nsw, nfw, g, g.n_phys_pages, (const float*)mu);
+                     chunk_id, ws, nfw, g, g.n_phys_pages, (const float*)mu);
 }
 
 // Entry i of the list: the i-th page of the concatenated ranges.
