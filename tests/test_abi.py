@@ -110,6 +110,9 @@ def test_kv_argument_errors():
                                  None) == nv.ESHAPE
     assert lib.nvfp4_kv_quantize(ctypes.byref(good), 0, 0, 16, 16, 7200, 0, 256, 1 << 20,
                                  None) == nv.ESHAPE
+    # a start token so large that start + T would overflow int64
+    assert lib.nvfp4_kv_quantize(ctypes.byref(good), 0, 0, 16, 16, 7040, (1 << 63) - 100, 256,
+                                 1 << 20, None) == nv.ESHAPE
     # a chunk after the first shorter than a page
     assert lib.nvfp4_kv_quantize(ctypes.byref(good), 0, 1, 16, 16, 100, 256, 256, 1 << 20,
                                  None) == nv.ESHAPE
@@ -163,6 +166,14 @@ def test_window_pages_host_side():
     assert (n.value, last.value) == (0, 0)
     # the list would not fit: rejected before any launch
     assert lib.nvfp4_kv_window_pages(65536, 256, 1024, 0, 0, 16384, 16, 67, ctypes.byref(n),
+                                     ctypes.byref(last), None) == nv.ESHAPE
+    # shot ranges whose end would overflow int64 are clipped to the cache first:
+    # a shot starting past the end contributes nothing ...
+    assert lib.nvfp4_kv_window_pages(100, 64, 0, (1 << 63) - 10, 100, 0, None, 0,
+                                     ctypes.byref(n), ctypes.byref(last), None) == nv.OK
+    assert (n.value, last.value) == (0, 0)
+    # ... and an endless shot from token 50 covers pages 0 and 1 (too many for one entry)
+    assert lib.nvfp4_kv_window_pages(100, 64, 0, 50, (1 << 63) - 1, 0, 16, 1, ctypes.byref(n),
                                      ctypes.byref(last), None) == nv.ESHAPE
     # bad sizes and missing outputs
     assert lib.nvfp4_kv_window_pages(100, 0, 0, 0, 0, 0, 16, 8, ctypes.byref(n),

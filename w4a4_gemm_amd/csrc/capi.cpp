@@ -228,8 +228,9 @@ int nvfp4_kv_quantize(const nvfp4_kv_cache_t* cache, int32_t layer, int32_t chun
   if (!aligned(k_bf16, 16) || !aligned(v_bf16, 16)) return NVFP4_ESHAPE;
   if (chunk_id < 0 || chunk_id >= cache->max_chunks) return NVFP4_ESHAPE;
   if (T < cache->page_tokens && chunk_id != 0) return NVFP4_ESHAPE;
-  if ((start_token + T + cache->page_tokens - 1) / cache->page_tokens > cache->max_pages)
-    return NVFP4_ESHAPE;
+  // the token range must end inside the layer's logical pages (no overflow)
+  const int64_t layer_tokens = (int64_t)cache->max_pages * cache->page_tokens;
+  if (start_token > layer_tokens || T > layer_tokens - start_token) return NVFP4_ESHAPE;
   // the general quantize kernel runs one workgroup per >= 64 tokens on grid.x
   if (T >= (int64_t(1) << 30)) return NVFP4_ESHAPE;
   const size_t need = nvfp4::kv_quantize_workspace_bytes(T, cache->n_heads, cache->head_dim);
@@ -300,8 +301,13 @@ int nvfp4_kv_window_pages(int64_t total_tokens, int32_t page_tokens, int64_t glo
   // the three token ranges, clipped, as page ranges [a, b)
   int64_t ra[3], rb[3];
   int n = 0;
+  // (sums clipped to total_tokens before they could overflow)
+  const int64_t shot_end = shot_start >= total_tokens ? total_tokens
+                         : shot_sink_tokens > total_tokens - shot_start
+                             ? total_tokens
+                             : shot_start + shot_sink_tokens;
   const int64_t tok[3][2] = {{0, global_sink_tokens},
-                             {shot_start, shot_start + shot_sink_tokens},
+                             {shot_start, shot_end},
                              {total_tokens - window_tokens, total_tokens}};
   for (int i = 0; i < 3; ++i) {
     const int64_t a = tok[i][0] < 0 ? 0 : tok[i][0];
