@@ -107,7 +107,7 @@ size_t nvfp4_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c);
  *   workspace  nvfp4_workspace_bytes(NVFP4_OP_QUANTIZE, rows, cols, amax != NULL)
  * rows == 0 is a no-op (s_g is still written: 1.0).
  * Errors: EINVAL (nulls, dtype), ESHAPE (cols % 16, alignment, tiled layout
- * with rows % 128 or cols % 64, ld_x < cols), EWORKSPACE. */
+ * with rows % 128 or cols % 64, ld_x < cols or ld_x > 2^40), EWORKSPACE. */
 int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                    const float* amax, const nvfp4_tensor_t* out, void* workspace,
                    size_t ws_bytes, void* stream);
@@ -131,7 +131,7 @@ int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, i
  *   workspace  nvfp4_workspace_bytes(NVFP4_OP_QUANTIZE, rows, cols, amax != NULL)
  * rows == 0 or cols == 0: only s_g (1.0, or from amax) is written.
  * Errors: EINVAL (nulls, dtype), ESHAPE (cols % 16, out dims, alignment,
- * ld_x < cols), EWORKSPACE. */
+ * ld_x < cols or ld_x > 2^40), EWORKSPACE. */
 int nvfp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
                               int64_t ld_x, const float* amax, const nvfp4_tensor_t* out,
                               void* workspace, size_t ws_bytes, void* stream);
@@ -186,7 +186,7 @@ int nvfp4_dequantize(const nvfp4_tensor_t* in, void* y, int32_t y_dtype, int64_t
  *           into (atomic max; initialise it to 0 before the first GEMM whose
  *           amax it should hold).  Lets the next quantize read Y once.
  * M == 0 or N == 0 is a no-op.
- * Errors: EINVAL, ESHAPE (K mismatch, ld_y). */
+ * Errors: EINVAL, ESHAPE (K mismatch, ld_y < N or ld_y > 2^40). */
 int nvfp4_gemm_w4a4(const nvfp4_tensor_t* x, const nvfp4_tensor_t* w, void* y, int32_t y_dtype,
                     int64_t ld_y, float* y_amax, void* stream);
 

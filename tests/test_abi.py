@@ -69,6 +69,9 @@ def test_argument_errors_return_before_launch():
     # missing workspace
     assert lib.nvfp4_quantize(16, nv.BF16, 128, 64, 64, None, ctypes.byref(good), None, 0,
                               None) == nv.EWORKSPACE
+    # a row stride beyond any tensor (it would overflow once scaled by the element size)
+    assert lib.nvfp4_quantize(16, nv.BF16, 128, 64, 1 << 62, None, ctypes.byref(good), 256, 4096,
+                              None) == nv.ESHAPE
     # ld_x < cols
     assert lib.nvfp4_quantize(16, nv.BF16, 128, 64, 32, None, ctypes.byref(good), 256, 4096,
                               None) == nv.ESHAPE

@@ -30,6 +30,14 @@ inline hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 // rows and one grid dimension holds fewer than 2^32 work-items.
 constexpr int64_t kMaxCols = int64_t(65535) * 128;
 constexpr int64_t kMaxRows = int64_t(1) << 28;
+// Row strides (elements) beyond any addressable tensor are rejected before they
+// are multiplied by an element size.
+constexpr int64_t kMaxLd = int64_t(1) << 40;
+
+// A row stride: at least `cols`, at most kMaxLd, rows 16-byte aligned.
+inline bool stride_ok(int64_t ld, int64_t cols, int64_t elem) {
+  return ld >= cols && ld <= kMaxLd && (ld * elem) % 16 == 0;
+}
 
 int check_tensor(const nvfp4_tensor_t* t) {
   if (!t) return NVFP4_EINVAL;
@@ -84,7 +92,7 @@ int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, i
   if (st) return st;
   if (out->rows != rows || out->cols != cols) return NVFP4_ESHAPE;
   const int64_t elem = x_dtype == NVFP4_BF16 ? 2 : 4;
-  if (ld_x < cols || (ld_x * elem) % 16) return NVFP4_ESHAPE;
+  if (!stride_ok(ld_x, cols, elem)) return NVFP4_ESHAPE;
   if (rows > 0 && cols > 0 && !x) return NVFP4_EINVAL;
   if (!aligned(x, 16)) return NVFP4_ESHAPE;
   if (amax && !aligned(amax, 4)) return NVFP4_ESHAPE;
@@ -107,7 +115,7 @@ int nvfp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t rows, int6
   if (out->rows != cols || out->cols != rows) return NVFP4_ESHAPE;
   if (cols % 16 || cols > kMaxCols) return NVFP4_ESHAPE;    // grid.y: 128 input columns each
   const int64_t elem = x_dtype == NVFP4_BF16 ? 2 : 4;
-  if (ld_x < cols || (ld_x * elem) % 16) return NVFP4_ESHAPE;
+  if (!stride_ok(ld_x, cols, elem)) return NVFP4_ESHAPE;
   if (rows > 0 && cols > 0 && !x) return NVFP4_EINVAL;
   if (!aligned(x, 16)) return NVFP4_ESHAPE;
   if (amax && !aligned(amax, 4)) return NVFP4_ESHAPE;
@@ -132,7 +140,7 @@ int nvfp4_adaln_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t c
   if (st) return st;
   if (out->rows != rows || out->cols != cols) return NVFP4_ESHAPE;
   const int64_t elem = x_dtype == NVFP4_BF16 ? 2 : 4;
-  if (ld_x < cols || (ld_x * elem) % 16) return NVFP4_ESHAPE;
+  if (!stride_ok(ld_x, cols, elem)) return NVFP4_ESHAPE;
   if (rows > 0 && cols > 0 && (!x || !shift || !scale || !row_stats)) return NVFP4_EINVAL;
   if (!aligned(x, 16) || !aligned(shift, 16) || !aligned(scale, 16) || !aligned(row_stats, 8))
     return NVFP4_ESHAPE;
@@ -152,7 +160,7 @@ int nvfp4_dequantize(const nvfp4_tensor_t* in, void* y, int32_t y_dtype, int64_t
   if (st) return st;
   if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_EINVAL;
   const int64_t elem = y_dtype == NVFP4_BF16 ? 2 : 4;
-  if (ld_y < in->cols || (ld_y * elem) % 16) return NVFP4_ESHAPE;
+  if (!stride_ok(ld_y, in->cols, elem)) return NVFP4_ESHAPE;
   if (in->rows > 0 && in->cols > 0 && !y) return NVFP4_EINVAL;
   if (!aligned(y, 16)) return NVFP4_ESHAPE;
   (void)hipGetLastError();
@@ -173,7 +181,7 @@ int nvfp4_gemm_w4a4(const nvfp4_tensor_t* x, const nvfp4_tensor_t* w, void* y, i
   const int64_t M = x->rows, N = w->rows, K = x->cols;
   // K % 16 == 0 (check_tensor); K % 64 != 0 implies row-major scales (a tiled
   // operand has cols % 64 == 0), which the GEMM's ragged-K path assumes
-  if (ld_y < N) return NVFP4_ESHAPE;
+  if (ld_y < N || ld_y > kMaxLd) return NVFP4_ESHAPE;
   if (M > 0 && N > 0 && !y) return NVFP4_EINVAL;
   if (!aligned(y, 4) || (y_amax && !aligned(y_amax, 4))) return NVFP4_ESHAPE;
   if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31)) return NVFP4_ESHAPE;
