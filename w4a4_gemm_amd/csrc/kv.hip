@@ -708,8 +708,11 @@ void launch_kv_quantize(const KvGeom& g, int32_t chunk_id, const uint16_t* k, co
                      g.page_bytes < (int64_t(1) << 32);
   if ((D == 64 || D == 128 || D == 256) && small) {
     const int64_t lanes = T * g.n_heads * (D / 8);
+    // at most one resident round of workgroups (256 CUs x 8 of 256 threads),
+    // each lane striding over several units: measured 11 % faster for a
+    // 7040-token chunk than 8192 short workgroups (too few waves stay resident)
     int64_t wgs = (lanes + 255) / 256;
-    wgs = wgs < 8192 ? wgs : 8192;                       // grid-stride beyond that
+    wgs = wgs < 2048 ? wgs : 2048;
     const auto go = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(256), 0, stream, k, v, T, start_token,
                          chunk_id, ws, nfw, g, g.n_phys_pages, (const float*)mu);
