@@ -377,11 +377,8 @@ static void launch_bn(const Operand& xa, const Operand& wb, const float* xg, con
   const int nbm = (int)((M + kBM - 1) / kBM), nbn = (int)((N + BN - 1) / BN);
   const size_t lds = 2 * (size_t)(2 * kBM) * kLdsRow * sizeof(uint16_t);
   auto kern = gemm_w4a4_kernel<BN, kOutBf16, kRag>;
-  // raise the dynamic-LDS limit once per instantiation (thread-safe static init)
-  static const bool configured =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds) == hipSuccess;
-  (void)configured;
+  static std::atomic<uint64_t> lds_done{0};         // per instantiation, per device
+  ensure_dynamic_lds((const void*)kern, (int)lds, lds_done);
   hipLaunchKernelGGL(kern, dim3((unsigned)(nbm * nbn)), dim3(kThreads), lds, stream, xa, wb, xg,
                      wg, (int)M, (int)N, K, y, ld_y, y_amax, nbm, nbn);
 }

@@ -434,11 +434,9 @@ void launch_kv_attention(const KvGeom& g, const int32_t* logical_pages, int32_t 
   const uint32_t q_sign = softmax_scale < 0.0f ? 0x80008000u : 0u;
   const int n_split = attention_splits(n_q, g.n_heads, (int64_t)n_pages * g.page_tokens);
   const dim3 grid((unsigned)((n_q + kQB - 1) / kQB), (unsigned)g.n_heads, (unsigned)n_split);
-  // dynamic LDS above the default 64 KB limit: raise it once (thread-safe static init)
-  static const bool configured =
-      hipFuncSetAttribute((const void*)kv_attention_kernel,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kAttnLds) == hipSuccess;
-  (void)configured;
+  // dynamic LDS above the default 64 KB limit, raised once per device
+  static std::atomic<uint64_t> lds_done{0};
+  ensure_dynamic_lds((const void*)kv_attention_kernel, (int)kAttnLds, lds_done);
   hipLaunchKernelGGL(kv_attention_kernel, grid, dim3(kThreads), kAttnLds, stream, g, g.n_phys_pages,
                      logical_pages, n_pages, last_page_tokens, q, n_q, scale_log2e, q_sign, out,
                      (float*)workspace, n_split);

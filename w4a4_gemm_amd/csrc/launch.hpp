@@ -7,7 +7,26 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace nvfp4 {
+
+// Raise `kernel`'s dynamic-LDS limit to `bytes` on the current device, once per
+// device: `done` is the calling launcher's own bit set (bit d: device d is
+// configured).  A failure is left to the launch, which then reports it.
+inline void ensure_dynamic_lds(const void* kernel, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return;
+  if (dev < 0 || dev >= 64) {                     // beyond the bit set: set it every time
+    (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    return;
+  }
+  const uint64_t bit = uint64_t(1) << dev;
+  if (done.load(std::memory_order_acquire) & bit) return;
+  if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) ==
+      hipSuccess)
+    done.fetch_or(bit, std::memory_order_release);
+}
 
 // ---- quantize / dequantize (quant.hip)
 constexpr int kAmaxPartials = 1024;   // partial maxima written by the amax pass (multiple of 256)
