@@ -266,9 +266,12 @@ def run_gpu(steps, warmup):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
 
-    # per-op durations from events on the launch stream (a separate, equal pass)
+    # per-op durations from events on the launch stream (a separate, equal pass);
+    # the steps are enqueued back to back and synchronised once, so no op's
+    # interval includes the host's launch latency after a synchronisation
     names = list(op_table())
     acc = {n: 0.0 for n in names}
+    per_step = []
     for _ in range(steps):
         evs = []
 
@@ -277,7 +280,9 @@ def run_gpu(steps, warmup):
             e.record()
             evs.append((name, e))
         wl.step(ev)
-        torch.cuda.synchronize()
+        per_step.append(evs)
+    torch.cuda.synchronize()
+    for evs in per_step:
         for (n, a), (_, b) in zip(evs[:-1], evs[1:]):
             acc[n] += a.elapsed_time(b) * 1e-3
     per_op = {n: acc[n] / steps for n in names}
