@@ -275,7 +275,7 @@ int nvfp4_kv_dequant_blocks(const nvfp4_kv_cache_t* cache, int32_t layer,
  *                  n_pages * page_tokens) bytes, 256-byte aligned: when few
  *                  (query block, head) pairs exist the window is split over
  *                  workgroups and their partial results meet there
- * Requires head_dim == 128 and page_tokens % 64 == 0.
+ * Requires head_dim 64 or 128 and page_tokens % 64 == 0.
  * Errors: EINVAL (nulls, negative sizes, last_page_tokens outside
  * [0, page_tokens] when n_pages > 0), ESHAPE (head_dim, page_tokens, layer,
  * alignment, n_heads > 65535), EWORKSPACE. */

@@ -137,9 +137,9 @@ def test_kv_attention_argument_errors():
     good = C(256, 28, 1, 24, 128, 256, 28, 2, 16, 16, 16, 16, 16)
     # nothing to do: no query rows
     assert lib.nvfp4_kv_attention(ctypes.byref(good), 0, 16, 4, 256, 16, 0, 0.1, 16, None, 0, None) == nv.OK
-    # head_dim other than 128, page_tokens not a multiple of 64
-    d64 = C(256, 28, 1, 24, 64, 256, 28, 2, 16, 16, 16, 16, 16)
-    assert lib.nvfp4_kv_attention(ctypes.byref(d64), 0, 16, 4, 256, 16, 8, 0.1, 16, None, 0, None) == nv.ESHAPE
+    # head_dim other than 64 or 128, page_tokens not a multiple of 64
+    d80 = C(256, 28, 1, 24, 80, 256, 28, 2, 16, 16, 16, 16, 16)
+    assert lib.nvfp4_kv_attention(ctypes.byref(d80), 0, 16, 4, 256, 16, 8, 0.1, 16, None, 0, None) == nv.ESHAPE
     p100 = C(256, 28, 1, 24, 128, 100, 28, 2, 16, 16, 16, 16, 16)
     assert lib.nvfp4_kv_attention(ctypes.byref(p100), 0, 16, 4, 100, 16, 8, 0.1, 16, None, 0, None) == nv.ESHAPE
     # last page token count out of range, negative sizes, null query / output

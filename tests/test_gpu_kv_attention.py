@@ -166,3 +166,31 @@ def test_long_context_window_full_size_sampled():
                              r.pages_per_layer)
     bound = 2.0 ** -7 * wabs + 2.0 ** -8 * np.abs(ref) + 1e-30
     assert float(np.max(np.abs(o[rows] - ref) / bound)) <= 1.0
+
+
+def test_head_dim_64_two_chunks_ragged_queries():
+    # head_dim 64: two chunks share page 1, logical page 7 (listed, never written)
+    # is unmapped, the last listed page is partial and 200 queries leave the
+    # second query block ragged
+    h, p, d = 3, 64, 64
+    table = np.array([[4, 0, 6, 2, 5, 1, 3, -1]], dtype=np.int32)
+    gpu, ora = _pair(h, p, 8, 2, table, 8, d=d)
+    kb, vb = synth.kv_chunk(t=400, h=h, d=d, seed_k=102, seed_v=103, seed_off=104)
+    _write(gpu, ora, 0, kb[:100], vb[:100], 0)              # chunk 0: page 0, 36 slots of page 1
+    _write(gpu, ora, 1, kb[100:400], vb[100:400], 100)      # chunk 1: rest of page 1 .. page 6
+    qb = synth.attn_queries(200, h, d, seed=105)
+    _check(gpu, ora, [0, 1, 2, 3, 7, 4, 5, 6], 400 - 6 * p, qb, 1 / math.sqrt(d), 8)
+    _check(gpu, ora, [3, 1, 0], p, qb, 0.2, 8)
+
+
+def test_head_dim_64_split_window():
+    # a one-block query grid over 24 pages: the window is split over workgroups
+    # and merged by the combine kernel (one channel per lane at head_dim 64)
+    h, p, d = 2, 64, 64
+    table = synth.page_permutation(24, 106)[None, :]
+    gpu, ora = _pair(h, p, 24, 1, table, 24, d=d)
+    assert nv.nvfp4_workspace_bytes(nv.OP_KV_ATTENTION, 40, h, 24 * p) > 0
+    kb, vb = synth.kv_chunk(t=24 * p, h=h, d=d, seed_k=107, seed_v=108, seed_off=109)
+    _write(gpu, ora, 0, kb, vb, 0)
+    qb = synth.attn_queries(40, h, d, seed=110)
+    _check(gpu, ora, list(range(24)), p, qb, 1 / math.sqrt(d), 24)

@@ -275,7 +275,8 @@ int nvfp4_kv_attention(const nvfp4_kv_cache_t* cache, int32_t layer,
   nvfp4::KvGeom g;
   int st = check_cache(cache, layer, &g);
   if (st) return st;
-  if (cache->head_dim != 128 || cache->page_tokens % 64) return NVFP4_ESHAPE;
+  if ((cache->head_dim != 64 && cache->head_dim != 128) || cache->page_tokens % 64)
+    return NVFP4_ESHAPE;
   // grid.y is the head; page offsets inside the kernel are 32-bit
   if (cache->n_heads > 65535 || g.page_bytes >= (int64_t(1) << 32)) return NVFP4_ESHAPE;
   if (n_pages < 0 || n_q < 0) return NVFP4_EINVAL;

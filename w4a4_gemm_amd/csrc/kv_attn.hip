@@ -20,6 +20,8 @@
 // from LDS in that same order.  Logits are scaled by scale * log2(e) and
 // exponentiated with exp2.
 
+#include <type_traits>
+
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -30,19 +32,27 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kD = 128;               // head_dim
 #ifndef NVFP4_ATTN_WAVES
 #define NVFP4_ATTN_WAVES 4
 #endif
 constexpr int kWaves = NVFP4_ATTN_WAVES;  // waves per workgroup, 32 queries each
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQB = 32 * kWaves;          // queries per workgroup
-constexpr int kKPT = 64 * 16 / kThreads;  // keys per thread in a block's decode
 constexpr int kKB = 64;               // keys per block
-constexpr int kKsRow = kD + 8;        // bf16 per K^ row in LDS (272 bytes: conflict-free reads)
 constexpr int kVtRow = kKB + 8;       // bf16 per V^T row in LDS (144 bytes)
-constexpr size_t kAttnLds =           // Q rows + K^ rows + V^T rows + K means (71,680 bytes)
-    2 * ((size_t)kQB * kKsRow + (size_t)kKB * kKsRow + (size_t)kD * kVtRow) + 2 * kD * 4;
+constexpr int kMaxD = 128;            // largest head_dim (sizes the split workspace)
+
+// Head-dim dependent shapes (head_dim kD = 64 or 128).
+template <int kD>
+struct Shape {
+  static constexpr int kGroups = kD / 8;                 // 8-channel units per key
+  static constexpr int kKPT = kKB * kGroups / kThreads;  // keys per thread in a block's decode
+  static constexpr int kKsRow = kD + 8;                  // bf16 per Q / K^ row in LDS (conflict-free)
+  static constexpr size_t kLds =                         // Q rows + K^ rows + V^T rows + K means
+      2 * ((size_t)kQB * kKsRow + (size_t)kKB * kKsRow + (size_t)kD * kVtRow) + 2 * kD * 4;
+  static_assert(kKPT == 2 || kKPT == 4, "a thread decodes 2 or 4 keys of a block");
+  static_assert(kThreads >= 2 * kD && kThreads == 2 * kQB, "thread roles of the Q and mean loads");
+};
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -81,24 +91,27 @@ __device__ __forceinline__ PageInfo page_info(const KvGeom& g, int64_t n_phys,
   return p;
 }
 
-// The raw inputs of one block for this thread: its units are the 4 adjacent
-// keys 4 (tid / 16) + i (i = 0..3) in channel group tid % 16 (the same 8
-// channels for every unit), written to V^T as 4-key runs.  The K means of the
-// page's two chunks (2 x 128 floats) travel one per thread and are shared
-// through LDS.
+// The raw inputs of one block for this thread: with G = kD / 8 channel groups
+// per key, its units are the kKPT adjacent keys kKPT (tid / G) + i in channel
+// group tid % G (the same 8 channels for every unit), written to V^T as
+// kKPT-key runs.  The K means of the page's two chunks (2 x kD floats) travel
+// one per thread and are shared through LDS.
+template <int kKPT>
 struct BlockRaw {
   uint32_t kc[kKPT], ks[kKPT], vc[kKPT], vs[kKPT];
-  float mu;               // K mean of chunk (tid < 128 ? c0 : c1), channel tid % 128 (tid < 256)
+  float mu;               // K mean of chunk (tid < kD ? c0 : c1), channel tid % kD (tid < 2 kD)
 };
 
+template <int kD>
 __device__ __forceinline__ void fetch_block(const KvGeom& g, const PageInfo& p, int h, int s0,
-                                            BlockRaw& r) {
+                                            BlockRaw<Shape<kD>::kKPT>& r) {
+  constexpr int kKPT = Shape<kD>::kKPT, kGroups = Shape<kD>::kGroups;
   // 32-bit offsets from the (uniform) page address: a page is far below 4 GiB
   const uint32_t H = g.n_heads, P = g.page_tokens;
   const uint32_t codes_region = H * P * (kD / 2);
   const uint32_t scales_region = H * P * (kD / 16);
-  const uint32_t sub = threadIdx.x & 15;
-  const uint32_t row0 = (uint32_t)h * P + s0 + kKPT * (threadIdx.x >> 4);
+  const uint32_t sub = threadIdx.x % kGroups;
+  const uint32_t row0 = (uint32_t)h * P + s0 + kKPT * (threadIdx.x / kGroups);
 #pragma unroll
   for (int i = 0; i < kKPT; ++i) {
     const uint32_t row = row0 + i;
@@ -116,12 +129,15 @@ __device__ __forceinline__ void fetch_block(const KvGeom& g, const PageInfo& p, 
 // 0, and zero values keep 0 * V^ finite whatever bytes the slot holds.
 // kSimple: the block is mapped, every slot holds a key and all belong to chunk
 // `cs` (uniform), so no per-key choice of chunk or mask is needed.
-template <bool kVCheck, bool kSimple>
+template <int kD, bool kVCheck, bool kSimple>
 __device__ __forceinline__ void decode_block(const PageInfo& p, int s0, int cs,
-                                             const BlockRaw& r, const float* __restrict__ Mu,
+                                             const BlockRaw<Shape<kD>::kKPT>& r,
+                                             const float* __restrict__ Mu,
                                              uint16_t* __restrict__ Ks,
                                              uint16_t* __restrict__ Vt) {
-  const int sub = threadIdx.x & 15;
+  constexpr int kKPT = Shape<kD>::kKPT, kGroups = Shape<kD>::kGroups;
+  constexpr int kKsRow = Shape<kD>::kKsRow;
+  const int sub = threadIdx.x % kGroups;
   const float* m0p = Mu + (kSimple ? cs * kD : 0) + 8 * sub;
   const f32x4 a0 = *(const f32x4*)m0p, b0 = *(const f32x4*)(m0p + 4);
   const float mu0[8] = {a0[0], a0[1], a0[2], a0[3], b0[0], b0[1], b0[2], b0[3]};
@@ -138,7 +154,7 @@ __device__ __forceinline__ void decode_block(const PageInfo& p, int s0, int cs,
   uint32_t vw[kKPT][4];                                     // V^ words of the thread's keys
 #pragma unroll
   for (int i = 0; i < kKPT; ++i) {
-    const int key = kKPT * (threadIdx.x >> 4) + i;
+    const int key = kKPT * (threadIdx.x / kGroups) + i;
     u32x4 ko, vo;
     if (kSimple) {
       kv_unit_bf16<kVCheck>(r.kc[i], r.ks[i], r.vc[i], r.vs[i], sgk_s, sgv_s, mu0, ko, vo);
@@ -157,7 +173,7 @@ __device__ __forceinline__ void decode_block(const PageInfo& p, int s0, int cs,
   }
   // V^T row 8 sub + c holds channel c of the 4 keys: bf16 of key i is the
   // low (c even) or high (c odd) half of vw[i][c / 2]
-  const int k0 = kKPT * (threadIdx.x >> 4);
+  const int k0 = kKPT * (threadIdx.x / kGroups);
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
@@ -202,7 +218,7 @@ int attention_splits(int64_t n_q, int64_t n_heads, int64_t n_keys) {
 size_t kv_attention_workspace_bytes(int64_t n_q, int64_t n_heads, int64_t n_keys) {
   const int s = attention_splits(n_q, n_heads, n_keys);
   if (s == 1) return 0;
-  return (size_t)s * n_q * n_heads * (kD + 2) * sizeof(float);
+  return (size_t)s * n_q * n_heads * (kMaxD + 2) * sizeof(float);
 }
 
 // Split `split` of `n_split` handles key blocks [b0, b1) of the window.  With
@@ -212,6 +228,7 @@ size_t kv_attention_workspace_bytes(int64_t n_q, int64_t n_heads, int64_t n_keys
 // O values.
 // Two workgroups per CU (registers capped at 256 per lane), so one
 // workgroup's decode overlaps the other's MFMAs.
+template <int kD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void kv_attention_kernel(KvGeom g, int64_t n_phys,
                                                            const int32_t* __restrict__ pages,
                                                            int n_pages, int last_tokens,
@@ -220,7 +237,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                                                            uint32_t q_sign,
                                                            uint16_t* __restrict__ out,
                                                            float* __restrict__ part, int n_split) {
-  // LDS (kAttnLds bytes, dynamic): Q rows, K^ rows, V^T rows, K means of chunk c0 then c1
+  // LDS (Shape<kD>::kLds bytes, dynamic): Q rows, K^ rows, V^T rows, K means of chunk c0 then c1
+  constexpr int kKsRow = Shape<kD>::kKsRow;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   uint16_t* Qs = smem;
   uint16_t* Ks = Qs + kQB * kKsRow;
@@ -232,17 +250,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int half = lane >> 5;
   const int64_t qrow = (int64_t)blockIdx.x * kQB + wave * 32 + (lane & 31);
 
-  // The workgroup's 128 query rows go to LDS once (two threads per row, 64
+  // The workgroup's 128 query rows go to LDS once (two threads per row, kD / 2
   // channels each); the first barrier of the block loop publishes them.  They
   // are the B operand of S^T = K^ Q^T: step s covers channels 16 s .. 16 s + 15,
   // lane half `half` the 8 channels 16 s + 8 half ..
   {
     const int row = tid >> 1;
     const int64_t qr = (int64_t)blockIdx.x * kQB + row;
-    const uint16_t* qp = q + ((qr < n_q ? qr : n_q - 1) * H + h) * kD + 64 * (tid & 1);
-    uint16_t* qs = Qs + row * kKsRow + 64 * (tid & 1);
+    const uint16_t* qp = q + ((qr < n_q ? qr : n_q - 1) * H + h) * kD + (kD / 2) * (tid & 1);
+    uint16_t* qs = Qs + row * kKsRow + (kD / 2) * (tid & 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kD / 16; ++i) {
       u32x4 v = *(const u32x4*)(qp + 8 * i);
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] ^= q_sign;           // -q when the scale is negative
@@ -263,18 +281,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // software pipeline: the raw inputs of block b + 1 are in flight while
   // block b is decoded and consumed
   PageInfo pn;
-  BlockRaw rn;
+  BlockRaw<Shape<kD>::kKPT> rn;
   if (b0 < b1) {
     pn = page_info(g, n_phys, pages, b0 / bpp, n_pages, last_tokens);
-    fetch_block(g, pn, h, (b0 % bpp) * kKB, rn);
+    fetch_block<kD>(g, pn, h, (b0 % bpp) * kKB, rn);
   }
   for (int b = b0; b < b1; ++b) {
     const int s0 = (b % bpp) * kKB;
     const PageInfo pc = pn;
-    const BlockRaw rc = rn;
+    const BlockRaw<Shape<kD>::kKPT> rc = rn;
     if (b + 1 < b1) {
       if ((b + 1) % bpp == 0) pn = page_info(g, n_phys, pages, (b + 1) / bpp, n_pages, last_tokens);
-      fetch_block(g, pn, h, ((b + 1) % bpp) * kKB, rn);
+      fetch_block<kD>(g, pn, h, ((b + 1) % bpp) * kKB, rn);
     }
     if (pc.valid <= s0) continue;                           // whole block masked (uniform)
     if (tid < 2 * kD) Mu[tid] = rc.mu;     // safe: the previous decode's reads of Mu
@@ -284,11 +302,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const bool simple = pc.mapped && s0 + kKB <= pc.valid && one_chunk;
       const int cs = s0 >= pc.split ? 1 : 0;
       if (simple) {
-        if (pc.vcheck) decode_block<true, true>(pc, s0, cs, rc, Mu, Ks, Vt);
-        else decode_block<false, true>(pc, s0, cs, rc, Mu, Ks, Vt);
+        if (pc.vcheck) decode_block<kD, true, true>(pc, s0, cs, rc, Mu, Ks, Vt);
+        else decode_block<kD, false, true>(pc, s0, cs, rc, Mu, Ks, Vt);
       } else {
-        if (pc.vcheck) decode_block<true, false>(pc, s0, 0, rc, Mu, Ks, Vt);
-        else decode_block<false, false>(pc, s0, 0, rc, Mu, Ks, Vt);
+        if (pc.vcheck) decode_block<kD, true, false>(pc, s0, 0, rc, Mu, Ks, Vt);
+        else decode_block<kD, false, false>(pc, s0, 0, rc, Mu, Ks, Vt);
       }
     }
     __syncthreads();
@@ -398,30 +416,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 // Merge the splits of one (query, head) row: M = max m_s, L = sum l_s 2^(m_s - M),
-// O = sum O_s 2^(m_s - M) / L, rounded once to bf16.  One wave per row, two
+// O = sum O_s 2^(m_s - M) / L, rounded once to bf16.  One wave per row, kD / 64
 // channels per lane.
+template <int kD>
 __global__ __launch_bounds__(256) void kv_attention_combine(const float* __restrict__ part,
                                                             int n_split, int64_t rows,
                                                             uint16_t* __restrict__ out) {
+  constexpr int kCpl = kD / 64;                             // channels per lane: 1 or 2
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
   const float* ml = part + (int64_t)n_split * rows * kD;
   float M = -__builtin_inff();
   for (int s = 0; s < n_split; ++s) M = fmaxf(M, ml[((int64_t)s * rows + row) * 2]);
-  float L = 0.0f, a0 = 0.0f, a1 = 0.0f;
+  float L = 0.0f, a[kCpl] = {};
   if (M != -__builtin_inff()) {
     for (int s = 0; s < n_split; ++s) {
       const f32x2 v = *(const f32x2*)(ml + ((int64_t)s * rows + row) * 2);
       const float w = __builtin_amdgcn_exp2f(v[0] - M);    // 0 for an empty split (m = -inf)
-      const f32x2 os = *(const f32x2*)(part + ((int64_t)s * rows + row) * kD + 2 * lane);
+      const float* os = part + ((int64_t)s * rows + row) * kD + kCpl * lane;
       L += v[1] * w;
-      a0 += os[0] * w;
-      a1 += os[1] * w;
+#pragma unroll
+      for (int c = 0; c < kCpl; ++c) a[c] += os[c] * w;
     }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  *(uint32_t*)(out + row * kD + 2 * lane) = pack_bf16x2(a0 * inv, a1 * inv);
+  if (kCpl == 2)
+    *(uint32_t*)(out + row * kD + 2 * lane) = pack_bf16x2(a[0] * inv, a[kCpl - 1] * inv);
+  else
+    out[row * kD + lane] = (uint16_t)f32_to_bf16_bits(a[0] * inv);
 }
 
 void launch_kv_attention(const KvGeom& g, const int32_t* logical_pages, int32_t n_pages,
@@ -434,17 +457,23 @@ void launch_kv_attention(const KvGeom& g, const int32_t* logical_pages, int32_t 
   const uint32_t q_sign = softmax_scale < 0.0f ? 0x80008000u : 0u;
   const int n_split = attention_splits(n_q, g.n_heads, (int64_t)n_pages * g.page_tokens);
   const dim3 grid((unsigned)((n_q + kQB - 1) / kQB), (unsigned)g.n_heads, (unsigned)n_split);
-  // dynamic LDS above the default 64 KB limit, raised once per device
-  static std::atomic<uint64_t> lds_done{0};
-  ensure_dynamic_lds((const void*)kv_attention_kernel, (int)kAttnLds, lds_done);
-  hipLaunchKernelGGL(kv_attention_kernel, grid, dim3(kThreads), kAttnLds, stream, g, g.n_phys_pages,
-                     logical_pages, n_pages, last_page_tokens, q, n_q, scale_log2e, q_sign, out,
-                     (float*)workspace, n_split);
-  if (n_split > 1) {
-    const int64_t rows = n_q * g.n_heads;
-    hipLaunchKernelGGL(kv_attention_combine, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
-                       stream, (const float*)workspace, n_split, rows, out);
-  }
+  const auto go = [&](auto d) {
+    constexpr int kD = decltype(d)::value;
+    constexpr size_t kLds = Shape<kD>::kLds;
+    // dynamic LDS above the default 64 KB limit (head_dim 128), raised once per device
+    static std::atomic<uint64_t> lds_done{0};
+    if (kLds > 65536) ensure_dynamic_lds((const void*)kv_attention_kernel<kD>, (int)kLds, lds_done);
+    hipLaunchKernelGGL(kv_attention_kernel<kD>, grid, dim3(kThreads), kLds, stream, g,
+                       g.n_phys_pages, logical_pages, n_pages, last_page_tokens, q, n_q,
+                       scale_log2e, q_sign, out, (float*)workspace, n_split);
+    if (n_split > 1) {
+      const int64_t rows = n_q * g.n_heads;
+      hipLaunchKernelGGL(kv_attention_combine<kD>, dim3((unsigned)((rows + 3) / 4)), dim3(256),
+                         0, stream, (const float*)workspace, n_split, rows, out);
+    }
+  };
+  if (g.head_dim == 64) go(std::integral_constant<int, 64>{});
+  else go(std::integral_constant<int, 128>{});
 }
 
 }  // namespace nvfp4
