@@ -248,3 +248,12 @@ def test_quantize_transposed_argument_errors():
     assert call(o=T(16, 16, 64, 64, 128, nv.SCALES_TILED)) == nv.ESHAPE   # tiled needs 128 | out rows
     wide = 65535 * 128 + 16                                   # beyond the grid's column tiles
     assert call(cols=wide, ld=wide, o=T(16, 16, 64, wide, 128, nv.SCALES_ROWMAJOR)) == nv.ESHAPE
+
+
+def test_default_scale_layout():
+    import w4a4_gemm_amd as nv
+    # tiled where the shape allows it, row-major otherwise (the GEMM takes either)
+    assert nv.default_layout(4096, 3072) == nv.SCALES_TILED
+    assert nv.default_layout(880, 3072) == nv.SCALES_ROWMAJOR      # rows % 128
+    assert nv.default_layout(256, 48) == nv.SCALES_ROWMAJOR        # cols % 64
+    assert nv.default_layout(0, 64) == nv.SCALES_TILED

@@ -99,7 +99,8 @@ def test_wgrad_over_ragged_token_count(bf16_out):
     dy = synth.weights_bf16(m, n, seed=33, std=1e-3)
     x64, dy64 = F.bf16_bits_to_f64(x), F.bf16_bits_to_f64(dy)
     a = nv.nvfp4_quantize_transposed(bf16_tensor(dy), layout=nv.SCALES_ROWMAJOR)
-    b = nv.nvfp4_quantize_transposed(bf16_tensor(x), layout=nv.SCALES_ROWMAJOR)
+    b = nv.nvfp4_quantize_transposed(bf16_tensor(x))    # default layout: row-major here
+    assert b.layout == nv.SCALES_ROWMAJOR
     dw = nv.nvfp4_gemm_w4a4(a, b, dtype=torch.bfloat16 if bf16_out else torch.float32)
     ya, yb = T.quantize_transposed(dy64), T.quantize_transposed(x64)
     assert_same_nvfp4(to_oracle(a), ya)

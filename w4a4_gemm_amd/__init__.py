@@ -23,7 +23,7 @@ __all__ = [
     "nvfp4_quantize_transposed",
     "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks", "nvfp4_kv_attention", "nvfp4_kv_window_pages",
     "SCALES_ROWMAJOR", "SCALES_TILED", "OP_QUANTIZE", "OP_KV_QUANTIZE", "OP_KV_ATTENTION",
-    "OP_ADALN_QUANTIZE",
+    "OP_ADALN_QUANTIZE", "default_layout",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so")
@@ -168,11 +168,20 @@ class NVFP4Tensor:
         return self.rows, self.cols
 
 
-def nvfp4_quantize(x, layout=SCALES_TILED, amax=None, out=None, workspace=None, stream=None):
-    """Quantize a 2-D bf16/fp32 CUDA tensor (row stride x.stride(0)) to NVFP4."""
+def default_layout(rows, cols):
+    """The tiled scale layout where the shape allows it (rows % 128 == 0 and
+    cols % 64 == 0), else row-major; the GEMM takes either."""
+    return SCALES_TILED if rows % 128 == 0 and cols % 64 == 0 else SCALES_ROWMAJOR
+
+
+def nvfp4_quantize(x, layout=None, amax=None, out=None, workspace=None, stream=None):
+    """Quantize a 2-D bf16/fp32 CUDA tensor (row stride x.stride(0)) to NVFP4
+    (``layout`` None: default_layout of the shape)."""
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     rows, cols = x.shape
+    if layout is None:
+        layout = default_layout(rows, cols)
     if out is None:
         out = NVFP4Tensor(rows, cols, layout, device=x.device)
     need = nvfp4_workspace_bytes(OP_QUANTIZE, rows, cols, 1 if amax is not None else 0)
@@ -186,12 +195,15 @@ def nvfp4_quantize(x, layout=SCALES_TILED, amax=None, out=None, workspace=None, 
     return out
 
 
-def nvfp4_quantize_transposed(x, layout=SCALES_TILED, amax=None, out=None, workspace=None,
+def nvfp4_quantize_transposed(x, layout=None, amax=None, out=None, workspace=None,
                               stream=None):
-    """NVFP4 of x^T (blocks of 16 along x's rows) for a 2-D bf16/fp32 CUDA tensor."""
+    """NVFP4 of x^T (blocks of 16 along x's rows) for a 2-D bf16/fp32 CUDA tensor
+    (``layout`` None: default_layout of the [cols x rows] output)."""
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     rows, cols = x.shape
+    if layout is None:
+        layout = default_layout(cols, rows)
     if out is None:
         out = NVFP4Tensor(cols, rows, layout, device=x.device)
     need = nvfp4_workspace_bytes(OP_QUANTIZE, rows, cols, 1 if amax is not None else 0)
@@ -206,7 +218,7 @@ def nvfp4_quantize_transposed(x, layout=SCALES_TILED, amax=None, out=None, works
     return out
 
 
-def nvfp4_adaln_quantize(x, shift, scale, rows_per_group, eps=1e-6, layout=SCALES_TILED,
+def nvfp4_adaln_quantize(x, shift, scale, rows_per_group, eps=1e-6, layout=None,
                          out=None, row_stats=None, workspace=None, stream=None):
     """LayerNorm + adaLN modulate + NVFP4 of a 2-D bf16/fp32 CUDA tensor -> (NVFP4Tensor, row_stats).
 
@@ -218,6 +230,8 @@ def nvfp4_adaln_quantize(x, shift, scale, rows_per_group, eps=1e-6, layout=SCALE
         if v.dtype != torch.float32 or not v.is_contiguous():
             raise ValueError("shift and scale must be contiguous fp32")
     rows, cols = x.shape
+    if layout is None:
+        layout = default_layout(rows, cols)
     groups = -(-rows // rows_per_group) if rows_per_group > 0 else 0
     if rows and cols and (shift.shape != (groups, cols) or scale.shape != (groups, cols)):
         raise ValueError(f"shift/scale must be [{groups}, {cols}]")
