@@ -27,7 +27,7 @@
  *
  * Conventions of every call:
  *   - All pointers are device pointers unless marked (host).  The caller
- *     owns every buffer; the library allocates nothing and keeps no state.
+ *     owns every buffer; the library allocates nothing.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream) and never synchronise the host.  Outputs are valid once the
  *     stream has reached the call.
@@ -39,8 +39,10 @@
  *     cast of the quantized buffers corrupts them).
  *   - Non-finite inputs and amax < 2688 * 2^-126 are outside the contract:
  *     the outputs are unspecified, but no call reads or writes out of bounds.
- *   - Thread safety: there is no mutable library state; concurrent calls
- *     on different streams are safe when their buffers do not overlap.
+ *   - Thread safety: the only library state is a once-per-device flag per
+ *     kernel recording that its dynamic-LDS limit was raised (set atomically);
+ *     concurrent calls on different streams are safe when their buffers do not
+ *     overlap.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
