@@ -97,6 +97,32 @@ def test_ragged_k(m, n, k):
     assert am == float(np.max(np.abs(yb)))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_row_stride_mixed_whole_and_edge_tiles(dtype):
+    """Y written into a wider buffer (ld_y > N): wave tiles wholly inside Y and
+    tiles on its bottom and right edges in one launch, with max|Y| folded over
+    both; the padding columns stay untouched."""
+    rng = np.random.default_rng(12)
+    m, n, k, ld = 384, 448, 256, 480
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    w = rng.standard_normal((n, k)).astype(np.float32)
+    xq, wq = _operands_from_f32(x, w)
+    y_ref, a_ref = Q.gemm(xq, wq)
+    big = torch.full((m, ld), float("nan"), dtype=dtype, device=dev())
+    am = torch.zeros(1, dtype=torch.float32, device=dev())
+    nv.nvfp4_gemm_w4a4(from_oracle(xq, nv.SCALES_TILED), from_oracle(wq, nv.SCALES_ROWMAJOR),
+                       dtype, out=big[:, :n], y_amax=am)
+    torch.cuda.synchronize()
+    full = big.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isnan(full[:, n:]))
+    y = full[:, :n]
+    if dtype == torch.float32:
+        assert Q.check_gemm_f32(y, y_ref, a_ref)[0]
+    else:
+        assert Q.check_gemm_bf16(y, y_ref, a_ref)[0]
+    assert float(am.cpu()[0]) == float(np.max(np.abs(y)))
+
+
 def test_empty_k_gives_zeros():
     """K == 0: the sum over k is empty, so Y = 0 (and max|Y| = 0)."""
     xq = Q.quantize(np.zeros((70, 0)))

@@ -263,8 +263,8 @@ __device__ __forceinline__ void gemm_step(f32x16 (&acc)[TM][TN], Frags<TM, TN, W
 
 // One 32 x 32 accumulator tile to Y (lane: column lane % 32; register r:
 // row (r / 4) * 8 + (lane / 32) * 4 + r % 4), also folding max |Y| as stored.
-// Every element is bounds-checked (measured faster here than a separate
-// unchecked path for whole tiles).
+// Every element is bounds-checked: the path for wave tiles that straddle an
+// edge of Y.
 template <bool kOutBf16>
 __device__ __forceinline__ void store_tile(const f32x16& a, float scale, void* y, int64_t ld_y,
                                            int row0, int col0, int M, int N, int lane,
@@ -284,6 +284,31 @@ __device__ __forceinline__ void store_tile(const f32x16& a, float scale, void* y
         ((float*)y)[(int64_t)row * ld_y + col] = v;
         amax = fmaxf(amax, __builtin_fabsf(v));
       }
+    }
+  }
+}
+
+// The same store for a 32 x 32 tile that lies inside Y.  base is the tile's
+// first element (wave-uniform, so the row addresses are formed on the scalar
+// unit) and off[r] the lane's byte offset of register r's element, which fits
+// 32 bits.  Per element that leaves the scale multiply, half a packed bf16
+// conversion, half a max3 and the store.  m folds max |acc * scale| before the
+// bf16 rounding: rounding is monotone and odd, so the largest stored magnitude
+// is m rounded (done once per wave).
+template <bool kOutBf16>
+__device__ __forceinline__ void store_tile_whole(const f32x16& a, float scale, char* base,
+                                                 const uint32_t (&off)[16], float& m) {
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    const float v0 = a[r] * scale, v1 = a[r + 1] * scale;
+    m = fmaxf(m, fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1)));
+    if (kOutBf16) {
+      const uint32_t pk = pack_bf16x2(v0, v1);
+      *(uint16_t*)(base + (uint64_t)off[r]) = (uint16_t)pk;
+      *(uint16_t*)(base + (uint64_t)off[r + 1]) = (uint16_t)(pk >> 16);
+    } else {
+      *(float*)(base + (uint64_t)off[r]) = v0;
+      *(float*)(base + (uint64_t)off[r + 1]) = v1;
     }
   }
 }
@@ -355,17 +380,38 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_kernel(
 
   // epilogue: Y = acc * (s_gx s_gw), rounded once to the output type
   const float scale = (*xg) * (*wg);
+  constexpr int kEs = kOutBf16 ? 2 : 4;            // bytes per Y element
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int row_w = tm * kBM + (wave_u >> 1) * 128, col_w = tn * BN + (wave_u & 1) * WN;
+  // whole wave tile inside Y, and every lane offset below 2^32 bytes
+  const bool whole = row_w + 128 <= M && col_w + WN <= N && ld_y * kEs <= (int64_t(1) << 27);
   float amax = 0.0f;
+  if (whole) {
+    const int64_t ldb = ld_y * kEs;
+    uint32_t off[16];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+    for (int r = 0; r < 16; ++r)
+      off[r] = (uint32_t)(((lane >> 5) * 4 + (r >> 2) * 8 + (r & 3)) * ldb + (lane & 31) * kEs);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int row0 = tm * kBM + wm * 128 + i * 32, col0 = tn * BN + wn * WN + j * 32;
-      store_tile<kOutBf16>(acc[i][j], scale, y, ld_y, row0, col0, M, N, lane, amax);
+    for (int i = 0; i < TM; ++i) {
+      char* base = (char*)y + ((int64_t)(row_w + i * 32) * ld_y + col_w) * kEs;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        store_tile_whole<kOutBf16>(acc[i][j], scale, base + j * 32 * kEs, off, amax);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int row0 = tm * kBM + wm * 128 + i * 32, col0 = tn * BN + wn * WN + j * 32;
+        store_tile<kOutBf16>(acc[i][j], scale, y, ld_y, row0, col0, M, N, lane, amax);
+      }
     }
   }
   if (y_amax) {
     amax = wave_max(amax);
+    if (kOutBf16 && whole) amax = __uint_as_float(f32_to_bf16_bits(amax) << 16);
     if (lane == 0) atomicMax((unsigned int*)y_amax, __float_as_uint(amax));
   }
 }
