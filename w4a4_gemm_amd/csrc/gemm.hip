@@ -29,6 +29,9 @@
 //   * Workgroups are remapped so that each of the 8 XCDs owns a contiguous run
 //     of tiles (better L2 reuse of shared X rows / W rows), grouped 8 tile
 //     rows at a time.
+//   * Epilogue: a wave tile inside Y is stored with row addresses formed on
+//     the scalar unit and a 32-bit offset per lane (three VALU instructions
+//     per two bf16 values); tiles on Y's edges check every element.
 
 #include <type_traits>
 
