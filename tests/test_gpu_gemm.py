@@ -200,6 +200,37 @@ def test_attn_proj_full_size_sampled():
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("stage", ["gemm1", "gemm2"])
+def test_ffn_full_size_sampled(stage):
+    """The FFN pair's launches as the benchmark runs them (GEMM1 8192 x 14336 x 3072
+    on 256-wide tiles, 1792 workgroups; GEMM2 8192 x 3072 x 14336 on 192-wide tiles,
+    512 workgroups), tiled scales, bf16 out with the fused max|Y|: 4096 sampled
+    outputs plus tile corners against exact dot products, and max|Y| against the
+    whole output."""
+    d = synth.ffn_pair()
+    if stage == "gemm1":
+        aq = Q.quantize(F.bf16_bits_to_f64(d["x"]))
+        bq = Q.quantize(F.bf16_bits_to_f64(d["w1"]))
+    else:
+        # stands in for the requantized Y1: N(0, 1) activations of its shape
+        y1 = synth.to_bf16_bits(synth.normal_f32((8192, 14336), 1.0, 24))
+        aq = Q.quantize(F.bf16_bits_to_f64(y1))
+        bq = Q.quantize(F.bf16_bits_to_f64(d["w2"]))
+    y, amax = _run(aq, bq, torch.bfloat16, amax=True)
+    print(f"[ffn {stage} full size] device done", flush=True)
+    m, n = y.shape
+    rng = np.random.default_rng(5)
+    rows = rng.integers(0, m, 4096)
+    cols = rng.integers(0, n, 4096)
+    rows[:8] = [0, 0, m - 1, m - 1, 255, 256, 127, 128]
+    cols[:8] = [0, n - 1, 0, n - 1, 255, 256, 191, 192]
+    y_ref, a_ref = Q.gemm_pairs(aq, bq, rows, cols)
+    ok, n_clause, n_fail = Q.check_gemm_bf16(y[rows, cols], y_ref, a_ref)
+    assert ok, (n_clause, n_fail)
+    assert amax == float(np.max(np.abs(y)))
+
+
+@pytest.mark.slow
 def test_ffn_stage_parity():
     """FFN pair, reduced M: GEMM1 -> requant with the fused amax -> GEMM2, each stage
     on oracle-made inputs; the chain on the device checked by properties."""
