@@ -233,12 +233,15 @@ int64_t nvfp4_kv_page_bytes(int32_t n_heads, int32_t head_dim, int32_t page_toke
  *   K', V quantized along head_dim and stored in place in their pages;
  *   k_mean / k_gscale / v_gscale / page_chunk updated.
  * Chunks of a layer are written in order, chunk c + 1 starting where chunk
- * c ended (so a page holds at most two chunks).  The page table entries for
+ * c ended (so a page holds at most two chunks); chunk 0 starts on a page
+ * boundary.  A chunk c > 0 that starts inside a page records that page's
+ * earlier slots as chunk c - 1's.  The page table entries for
  * the touched pages must be valid physical pages.  The mean is accumulated in
  * fp64 in a fixed order; it is exact while the partial sums of a channel stay
  * within fp64's 53 bits (true for bf16 data of moderate dynamic range).
- * Errors: EINVAL, ESHAPE (T < page_tokens unless it is chunk 0, T >= 2^30,
- * head_dim, token range past max_pages, chunk_id >= max_chunks), EWORKSPACE. */
+ * Errors: EINVAL, ESHAPE (T < page_tokens unless it is chunk 0, chunk 0 not
+ * starting on a page boundary, T >= 2^30, head_dim, token range past
+ * max_pages, chunk_id >= max_chunks), EWORKSPACE. */
 int nvfp4_kv_quantize(const nvfp4_kv_cache_t* cache, int32_t layer, int32_t chunk_id,
                       const void* k_bf16, const void* v_bf16, int64_t T, int64_t start_token,
                       void* workspace, size_t ws_bytes, void* stream);
@@ -309,9 +312,11 @@ int nvfp4_kv_window_pages(int64_t total_tokens, int32_t page_tokens, int64_t glo
                           int32_t* pages_dev, int32_t max_pages, int32_t* n_pages,
                           int32_t* last_page_tokens, void* stream);
 
-/* Library version and messages. */
+/* Library version and messages.  nvfp4_source_hash: sha256 (hex) of the
+ * sources the library was built from, as computed by the build script. */
 int nvfp4_abi_version(void);
 const char* nvfp4_status_string(int status);
+const char* nvfp4_source_hash(void);
 
 #ifdef __cplusplus
 }

@@ -124,6 +124,10 @@ class KVPool:
 
     def write_chunk(self, layer, chunk_id, k, v, start_token) -> ChunkQ:
         """Quantize one chunk and store it in place (pages, mu, scales, page_chunk)."""
+        if chunk_id == 0 and start_token % self.P:
+            # a chunk that starts inside a page shares it with the chunk before
+            # it; the first chunk of a layer has none
+            raise ValueError("chunk 0 must start on a page boundary")
         c = ChunkQ(k, v)
         t = k.shape[0]
         self.k_mean[layer, chunk_id] = c.mu
@@ -141,7 +145,9 @@ class KVPool:
         last = (start_token + t - 1) // self.P
         for lp in range(first, last + 1):
             if lp == first and start_token % self.P:
-                self.page_chunk[layer, lp, 1] = start_token % self.P
+                # slots before the chunk's first token belong to the chunk
+                # written just before it (chunks of a layer are written in order)
+                self.page_chunk[layer, lp] = (chunk_id - 1, start_token % self.P)
             else:
                 self.page_chunk[layer, lp] = (chunk_id, self.P)
         return c

@@ -31,6 +31,16 @@ def test_library_exports_every_declared_symbol():
     assert set(nv.EXPORTS) <= set(_declared_functions())
 
 
+def test_library_was_built_from_these_sources():
+    import importlib.util
+    import w4a4_gemm_amd as nv
+    spec = importlib.util.spec_from_file_location(
+        "srchash", os.path.join(ROOT, "w4a4_gemm_amd", "srchash.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert nv._lib.nvfp4_source_hash().decode() == mod.source_hash()
+
+
 def test_version_and_status_strings():
     import w4a4_gemm_amd as nv
     assert nv.nvfp4_abi_version() == 1
@@ -118,6 +128,10 @@ def test_kv_argument_errors():
                                  1 << 20, None) == nv.ESHAPE
     # a chunk after the first shorter than a page
     assert lib.nvfp4_kv_quantize(ctypes.byref(good), 0, 1, 16, 16, 100, 256, 256, 1 << 20,
+                                 None) == nv.ESHAPE
+    # the first chunk of a layer starting inside a page (its earlier slots would
+    # belong to no chunk)
+    assert lib.nvfp4_kv_quantize(ctypes.byref(good), 0, 0, 16, 16, 300, 100, 256, 1 << 20,
                                  None) == nv.ESHAPE
     # workspace too small
     assert lib.nvfp4_kv_quantize(ctypes.byref(good), 0, 0, 16, 16, 7040, 0, 256, 16,

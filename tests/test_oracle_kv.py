@@ -76,6 +76,22 @@ def test_page_chunk_metadata_for_straddling_writes():
     assert pool.page_chunk[1, 2].tolist() == [1, 16]
 
 
+def test_page_chunk_metadata_does_not_depend_on_stale_entries():
+    # a chunk starting inside a page records the page's earlier slots as the
+    # previous chunk's, whatever the table held before; chunk 0 cannot start
+    # inside a page (its earlier slots would belong to no chunk)
+    rng = np.random.default_rng(3)
+    pool = _small_pool(rng)
+    pool.page_chunk[0] = 2                           # stale entries from an earlier use
+    kb, vb = synth.kv_chunk(t=40, h=2, d=32, seed_k=5, seed_v=6, seed_off=7)
+    k, v = F.bf16_bits_to_f64(kb), F.bf16_bits_to_f64(vb)
+    pool.write_chunk(0, 0, k[:24], v[:24], 0)
+    pool.write_chunk(0, 1, k[24:], v[24:], 24)
+    assert pool.page_chunk[0, :3].tolist() == [[0, 16], [0, 8], [1, 16]]
+    with pytest.raises(ValueError):
+        pool.write_chunk(1, 0, k[:24], v[:24], 5)
+
+
 def test_dequant_matches_fraction_brute_force_and_is_shuffle_invariant():
     rng = np.random.default_rng(4)
     pool = _small_pool(rng, p=16)

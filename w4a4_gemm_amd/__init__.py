@@ -12,6 +12,7 @@ missing or broken library raises at import time.
 """
 
 import ctypes
+import importlib.util
 import os
 
 import torch
@@ -36,7 +37,8 @@ OP_QUANTIZE, OP_KV_QUANTIZE, OP_KV_ATTENTION, OP_ADALN_QUANTIZE = 0, 1, 2, 3
 ABI_VERSION = 1
 
 EXPORTS = (
-    "nvfp4_abi_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_kv_page_bytes",
+    "nvfp4_abi_version", "nvfp4_status_string", "nvfp4_source_hash", "nvfp4_workspace_bytes",
+    "nvfp4_kv_page_bytes",
     "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm_w4a4", "nvfp4_adaln_quantize",
     "nvfp4_quantize_transposed",
     "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks", "nvfp4_kv_attention", "nvfp4_kv_window_pages",
@@ -69,6 +71,7 @@ def _load():
     sig = {
         "nvfp4_abi_version": (ctypes.c_int, []),
         "nvfp4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "nvfp4_source_hash": (ctypes.c_char_p, []),
         "nvfp4_workspace_bytes": (sz, [i32, i64, i64, i64]),
         "nvfp4_kv_page_bytes": (i64, [i32, i32, i32]),
         "nvfp4_quantize": (ctypes.c_int, [vp, i32, i64, i64, i64, vp, ctypes.POINTER(_Tensor),
@@ -97,6 +100,15 @@ def _load():
         fn.restype, fn.argtypes = res, args
     if lib.nvfp4_abi_version() != ABI_VERSION:
         raise ImportError("libnvfp4.so ABI version mismatch: rebuild the library")
+    # the library must have been built from the sources next to it
+    spec = importlib.util.spec_from_file_location(
+        "nvfp4_srchash", os.path.join(os.path.dirname(LIB_PATH), "srchash.py"))
+    srchash = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(srchash)
+    want, got = srchash.source_hash(), lib.nvfp4_source_hash().decode()
+    if got != want:
+        raise ImportError(f"{LIB_PATH} was built from other sources (hash {got[:12]}, sources "
+                          f"{want[:12]}): rebuild it with `python w4a4_gemm_amd/build.py`")
     return lib
 
 
@@ -116,6 +128,37 @@ def _stream(stream=None):
 
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else ctypes.c_void_p(0)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_buffer(t, name, dtype, device, numel=None, shape=None):
+    """A caller-supplied buffer: its dtype, device, size and layout are checked
+    here because the C ABI sees only a pointer."""
+    _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _need(t.device == torch.device(device), f"{name} must be on {device}, got {t.device}")
+    if shape is not None:
+        _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got "
+              f"{tuple(t.shape)}")
+        _need(t.dim() == 0 or t.stride(-1) == 1 or t.numel() == 0,
+              f"{name} must have unit stride in its last dimension")
+    else:
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+        _need(t.numel() >= numel, f"{name} holds {t.numel()} elements, needs {numel}")
+
+
+def _check_nvfp4(t, name, device=None):
+    """An NVFP4Tensor's three buffers hold rows x cols codes, scale bytes and s_g."""
+    _need(isinstance(t, NVFP4Tensor), f"{name} must be an NVFP4Tensor")
+    device = t.global_scale.device if device is None else device
+    n = t.rows * t.cols
+    _check_buffer(t.codes, f"{name}.codes", torch.uint8, device, numel=n // 2)
+    _check_buffer(t.scales, f"{name}.scales", torch.uint8, device, numel=n // 16)
+    _check_buffer(t.global_scale, f"{name}.global_scale", torch.float32, device, numel=1)
 
 
 def _dtype_code(dt):
@@ -184,9 +227,14 @@ def nvfp4_quantize(x, layout=None, amax=None, out=None, workspace=None, stream=N
         layout = default_layout(rows, cols)
     if out is None:
         out = NVFP4Tensor(rows, cols, layout, device=x.device)
+    _check_nvfp4(out, "out", x.device)
+    if amax is not None:
+        _check_buffer(amax, "amax", torch.float32, x.device, numel=1)
     need = nvfp4_workspace_bytes(OP_QUANTIZE, rows, cols, 1 if amax is not None else 0)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        _check_buffer(workspace, "workspace", torch.uint8, x.device, numel=need)
     cs = out.c()
     st = _lib.nvfp4_quantize(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0),
                              _ptr(amax), ctypes.byref(cs), _ptr(workspace),
@@ -206,9 +254,14 @@ def nvfp4_quantize_transposed(x, layout=None, amax=None, out=None, workspace=Non
         layout = default_layout(cols, rows)
     if out is None:
         out = NVFP4Tensor(cols, rows, layout, device=x.device)
+    _check_nvfp4(out, "out", x.device)
+    if amax is not None:
+        _check_buffer(amax, "amax", torch.float32, x.device, numel=1)
     need = nvfp4_workspace_bytes(OP_QUANTIZE, rows, cols, 1 if amax is not None else 0)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        _check_buffer(workspace, "workspace", torch.uint8, x.device, numel=need)
     cs = out.c()
     st = _lib.nvfp4_quantize_transposed(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0),
                                         _ptr(amax), ctypes.byref(cs), _ptr(workspace),
@@ -237,11 +290,16 @@ def nvfp4_adaln_quantize(x, shift, scale, rows_per_group, eps=1e-6, layout=None,
         raise ValueError(f"shift/scale must be [{groups}, {cols}]")
     if out is None:
         out = NVFP4Tensor(rows, cols, layout, device=x.device)
+    _check_nvfp4(out, "out", x.device)
+    for v, name in ((shift, "shift"), (scale, "scale")):
+        _need(v.device == x.device, f"{name} must be on {x.device}")
     if row_stats is None:
         row_stats = torch.empty((rows, 2), dtype=torch.float32, device=x.device)
+    _check_buffer(row_stats, "row_stats", torch.float32, x.device, numel=2 * rows)
+    need = nvfp4_workspace_bytes(OP_ADALN_QUANTIZE, rows, cols, 0)
     if workspace is None:
-        workspace = torch.empty(nvfp4_workspace_bytes(OP_ADALN_QUANTIZE, rows, cols, 0),
-                                dtype=torch.uint8, device=x.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check_buffer(workspace, "workspace", torch.uint8, x.device, numel=need)
     cs = out.c()
     st = _lib.nvfp4_adaln_quantize(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0),
                                    _ptr(shift), _ptr(scale), rows_per_group, eps, _ptr(row_stats),
@@ -252,22 +310,33 @@ def nvfp4_adaln_quantize(x, shift, scale, rows_per_group, eps=1e-6, layout=None,
 
 
 def nvfp4_dequantize(t, dtype=torch.float32, out=None, stream=None):
+    """x^ = q s_b s_g of an NVFP4Tensor as fp32 or bf16 [rows x cols]; ``out``
+    may be a row-strided 2-D view."""
+    _check_nvfp4(t, "t")
     if out is None:
         out = torch.empty((t.rows, t.cols), dtype=dtype, device=t.codes.device)
+    _check_buffer(out, "out", out.dtype if out.dtype in (torch.float32, torch.bfloat16) else dtype,
+                  t.codes.device, shape=(t.rows, t.cols))
     cs = t.c()
     st = _lib.nvfp4_dequantize(ctypes.byref(cs), _ptr(out), _dtype_code(out.dtype),
-                               out.stride(0) if out.dim() == 2 else t.cols, _stream(stream))
+                               out.stride(0) if t.rows > 1 else t.cols, _stream(stream))
     _check(st, "nvfp4_dequantize")
     return out
 
 
 def nvfp4_gemm_w4a4(x, w, dtype=torch.bfloat16, out=None, y_amax=None, stream=None):
-    """Y = X W^T for NVFP4 X [M x K], W [N x K]."""
+    """Y = X W^T for NVFP4 X [M x K], W [N x K]; ``out`` may be a row-strided 2-D view."""
+    _check_nvfp4(x, "x")
+    _check_nvfp4(w, "w", x.codes.device)
     if out is None:
         out = torch.empty((x.rows, w.rows), dtype=dtype, device=x.codes.device)
+    _check_buffer(out, "out", out.dtype if out.dtype in (torch.float32, torch.bfloat16) else dtype,
+                  x.codes.device, shape=(x.rows, w.rows))
+    if y_amax is not None:
+        _check_buffer(y_amax, "y_amax", torch.float32, x.codes.device, numel=1)
     xs, ws = x.c(), w.c()
     st = _lib.nvfp4_gemm_w4a4(ctypes.byref(xs), ctypes.byref(ws), _ptr(out), _dtype_code(out.dtype),
-                              out.stride(0) if out.dim() == 2 else w.rows, _ptr(y_amax),
+                              out.stride(0) if x.rows > 1 else w.rows, _ptr(y_amax),
                               _stream(stream))
     _check(st, "nvfp4_gemm_w4a4")
     return out
@@ -318,7 +387,11 @@ def nvfp4_kv_quantize(cache, layer, chunk_id, k, v, start_token, workspace=None,
         raise ValueError("K and V must be contiguous [T, n_heads, head_dim] of the same shape")
     if tuple(k.shape[1:]) != (cache.n_heads, cache.head_dim):
         raise ValueError("K shape does not match the cache")
+    _need(k.device == cache.pool.device and v.device == cache.pool.device,
+          "K and V must be on the cache's device")
     ws = workspace if workspace is not None else cache.workspace(T)
+    _check_buffer(ws, "workspace", torch.uint8, cache.pool.device,
+                  numel=nvfp4_workspace_bytes(OP_KV_QUANTIZE, T, cache.n_heads, cache.head_dim))
     st = _lib.nvfp4_kv_quantize(ctypes.byref(cache.c()), layer, chunk_id, _ptr(k), _ptr(v), T,
                                 start_token, _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "nvfp4_kv_quantize")
@@ -326,12 +399,16 @@ def nvfp4_kv_quantize(cache, layer, chunk_id, k, v, start_token, workspace=None,
 
 def nvfp4_kv_dequant_blocks(cache, layer, logical_pages, k_out=None, v_out=None, stream=None):
     """Dequantize the listed logical pages -> (K^, V^) bf16 [n*page_tokens, H, D]."""
+    _check_buffer(logical_pages, "logical_pages", torch.int32, cache.pool.device, numel=0)
     n = logical_pages.numel()
     shape = (n * cache.page_tokens, cache.n_heads, cache.head_dim)
     if k_out is None:
         k_out = torch.empty(shape, dtype=torch.bfloat16, device=cache.pool.device)
     if v_out is None:
         v_out = torch.empty(shape, dtype=torch.bfloat16, device=cache.pool.device)
+    need = shape[0] * shape[1] * shape[2]
+    _check_buffer(k_out, "k_out", torch.bfloat16, cache.pool.device, numel=need)
+    _check_buffer(v_out, "v_out", torch.bfloat16, cache.pool.device, numel=need)
     st = _lib.nvfp4_kv_dequant_blocks(ctypes.byref(cache.c()), layer, _ptr(logical_pages), n,
                                       _ptr(k_out), _ptr(v_out), _stream(stream))
     _check(st, "nvfp4_kv_dequant_blocks")
@@ -345,12 +422,18 @@ def nvfp4_kv_attention(cache, layer, logical_pages, last_page_tokens, q, softmax
         raise TypeError("q must be contiguous bf16 [n_q, n_heads, head_dim]")
     if tuple(q.shape[1:]) != (cache.n_heads, cache.head_dim):
         raise ValueError("q must be [n_q, n_heads, head_dim]")
+    _need(q.device == cache.pool.device, "q must be on the cache's device")
     if out is None:
         out = torch.empty_like(q)
+    _check_buffer(out, "out", torch.bfloat16, q.device, numel=q.numel())
+    _need(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    _check_buffer(logical_pages, "logical_pages", torch.int32, q.device, numel=0)
     n = logical_pages.numel()
     need = nvfp4_workspace_bytes(OP_KV_ATTENTION, q.shape[0], cache.n_heads, n * cache.page_tokens)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _check_buffer(workspace, "workspace", torch.uint8, q.device, numel=need)
     st = _lib.nvfp4_kv_attention(ctypes.byref(cache.c()), layer, _ptr(logical_pages), n,
                                  last_page_tokens, _ptr(q), q.shape[0], float(softmax_scale),
                                  _ptr(out), _ptr(workspace),
@@ -372,6 +455,7 @@ def nvfp4_kv_window_pages(total_tokens, page_tokens, global_sink_tokens, shot_st
         pages = torch.empty(n_max, dtype=torch.int32, device=device)
     if max_pages is None:
         max_pages = pages.numel()
+    _check_buffer(pages, "pages", torch.int32, pages.device, numel=max_pages)
     n, last = ctypes.c_int32(0), ctypes.c_int32(0)
     st = _lib.nvfp4_kv_window_pages(total_tokens, page_tokens, global_sink_tokens, shot_start,
                                     shot_sink_tokens, window_tokens, _ptr(pages), max_pages,

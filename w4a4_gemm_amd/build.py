@@ -16,6 +16,7 @@ Run it as a script (or load it by path): importing the package loads the
 library and checks its symbols, which fails while the library is stale.
 """
 
+import importlib.util
 import os
 import subprocess
 import sys
@@ -57,15 +58,26 @@ def _run(cmd, verbose):
         print(err)
 
 
+def _source_hash():
+    spec = importlib.util.spec_from_file_location("nvfp4_srchash", os.path.join(HERE, "srchash.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.source_hash()
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libnvfp4.so; returns the library path."""
+    """Compile every source and link libnvfp4.so; returns the library path.
+    The library carries the hash of the sources it was built from
+    (nvfp4_source_hash), which the binding checks when it loads."""
     os.makedirs(BUILD, exist_ok=True)
     objs = []
     cmds = []
+    tag = [f"-DNVFP4_SOURCE_HASH=\"{_source_hash()}\""]
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmds.append([HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        extra = tag if src == "capi.cpp" else []
+        cmds.append([HIPCC, *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:

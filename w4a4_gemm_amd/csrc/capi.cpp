@@ -55,11 +55,32 @@ int check_tensor(const nvfp4_tensor_t* t) {
   return NVFP4_OK;
 }
 
+// Arguments of a quantize call other than its workspace.
+int check_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                   const float* amax, const nvfp4_tensor_t* out) {
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (rows < 0 || cols < 0) return NVFP4_EINVAL;
+  int st = check_tensor(out);
+  if (st) return st;
+  if (out->rows != rows || out->cols != cols) return NVFP4_ESHAPE;
+  const int64_t elem = x_dtype == NVFP4_BF16 ? 2 : 4;
+  if (!stride_ok(ld_x, cols, elem)) return NVFP4_ESHAPE;
+  if (rows > 0 && cols > 0 && !x) return NVFP4_EINVAL;
+  if (!aligned(x, 16)) return NVFP4_ESHAPE;
+  if (amax && !aligned(amax, 4)) return NVFP4_ESHAPE;
+  return NVFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+#ifndef NVFP4_SOURCE_HASH
+#define NVFP4_SOURCE_HASH "unknown"
+#endif
+const char* nvfp4_source_hash(void) { return NVFP4_SOURCE_HASH; }
 
 const char* nvfp4_status_string(int status) {
   switch (status) {
@@ -86,16 +107,8 @@ size_t nvfp4_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c) {
 int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                    const float* amax, const nvfp4_tensor_t* out, void* workspace,
                    size_t ws_bytes, void* stream) {
-  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_EINVAL;
-  if (rows < 0 || cols < 0) return NVFP4_EINVAL;
-  int st = check_tensor(out);
+  const int st = check_quantize(x, x_dtype, rows, cols, ld_x, amax, out);
   if (st) return st;
-  if (out->rows != rows || out->cols != cols) return NVFP4_ESHAPE;
-  const int64_t elem = x_dtype == NVFP4_BF16 ? 2 : 4;
-  if (!stride_ok(ld_x, cols, elem)) return NVFP4_ESHAPE;
-  if (rows > 0 && cols > 0 && !x) return NVFP4_EINVAL;
-  if (!aligned(x, 16)) return NVFP4_ESHAPE;
-  if (amax && !aligned(amax, 4)) return NVFP4_ESHAPE;
   const size_t need = nvfp4::quantize_workspace_bytes(rows, cols, amax != nullptr);
   if (need && (!workspace || ws_bytes < need || !aligned(workspace, 256))) return NVFP4_EWORKSPACE;
   (void)hipGetLastError();
@@ -236,6 +249,9 @@ int nvfp4_kv_quantize(const nvfp4_kv_cache_t* cache, int32_t layer, int32_t chun
   if (!aligned(k_bf16, 16) || !aligned(v_bf16, 16)) return NVFP4_ESHAPE;
   if (chunk_id < 0 || chunk_id >= cache->max_chunks) return NVFP4_ESHAPE;
   if (T < cache->page_tokens && chunk_id != 0) return NVFP4_ESHAPE;
+  // a chunk that starts inside a page shares it with the chunk before it, so
+  // the first chunk of a layer must start on a page boundary
+  if (chunk_id == 0 && start_token % cache->page_tokens != 0) return NVFP4_ESHAPE;
   // the token range must end inside the layer's logical pages (no overflow)
   const int64_t layer_tokens = (int64_t)cache->max_pages * cache->page_tokens;
   if (start_token > layer_tokens || T > layer_tokens - start_token) return NVFP4_ESHAPE;

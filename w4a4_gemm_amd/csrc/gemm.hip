@@ -1,6 +1,6 @@
 // W4A4 GEMM on gfx950: Y[M x N] = X[M x K] * W[N x K]^T, both operands NVFP4.
 //
-// "All matrix multiplications run in 4 bits" (techwalker.com LongLive-2.0
+// Every matmul of the model runs in 4-bit NVFP4 (techwalker.com LongLive-2.0
 // report summary, section 四, first key).  gfx950's scaled FP4 MFMA takes
 // power-of-two (E8M0) scales per 32 values, which cannot carry NVFP4's E4M3
 // scale per 16 values exactly.  Instead every product q s_b is formed exactly

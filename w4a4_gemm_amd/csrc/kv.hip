@@ -251,8 +251,9 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(
   // page -> chunk bookkeeping (one thread per touched page)
   if (h == 0 && grp == 0) {
     if (t == 0) {
-      if (slot) g.page_chunk[2 * lp + 1] = slot;
-      else { g.page_chunk[2 * lp] = chunk_id; g.page_chunk[2 * lp + 1] = P; }
+      // a chunk starting inside a page: the slots before it are chunk_id - 1's
+      g.page_chunk[2 * lp] = slot ? chunk_id - 1 : chunk_id;
+      g.page_chunk[2 * lp + 1] = slot ? (int32_t)slot : P;
     } else if (slot == 0) {
       g.page_chunk[2 * lp] = chunk_id;
       g.page_chunk[2 * lp + 1] = P;
@@ -655,8 +656,9 @@ __global__ __launch_bounds__(256) void kv_quantize_flat_kernel(
       // page -> chunk bookkeeping (one lane per touched page)
       if (in && h == 0 && j == 0) {
         if (t == 0) {
-          if (slot) g.page_chunk[2 * lp + 1] = slot;
-          else { g.page_chunk[2 * lp] = chunk_id; g.page_chunk[2 * lp + 1] = P; }
+          // a chunk starting inside a page: the slots before it are chunk_id - 1's
+          g.page_chunk[2 * lp] = slot ? chunk_id - 1 : chunk_id;
+          g.page_chunk[2 * lp + 1] = slot ? (int32_t)slot : (int32_t)P;
         } else if (slot == 0) {
           g.page_chunk[2 * lp] = chunk_id;
           g.page_chunk[2 * lp + 1] = P;
