@@ -39,10 +39,11 @@
  *     cast of the quantized buffers corrupts them).
  *   - Non-finite inputs and amax < 2688 * 2^-126 are outside the contract:
  *     the outputs are unspecified, but no call reads or writes out of bounds.
- *   - Thread safety: the only library state is a once-per-device flag per
- *     kernel recording that its dynamic-LDS limit was raised (set atomically);
- *     concurrent calls on different streams are safe when their buffers do not
- *     overlap.
+ *   - Thread safety: the library state is a once-per-device flag per kernel
+ *     recording that its dynamic-LDS limit was raised (set atomically) and the
+ *     per-device address of nvfp4_quantize_noalloc's scratch array (looked up
+ *     once under a lock); concurrent calls on different streams are safe when
+ *     their buffers do not overlap (nvfp4_quantize_noalloc: see there).
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -113,6 +114,22 @@ size_t nvfp4_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c);
 int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                    const float* amax, const nvfp4_tensor_t* out, void* workspace,
                    size_t ws_bytes, void* stream);
+
+/* nvfp4_quantize without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops that forbid allocation).
+ * Arguments and results are those of nvfp4_quantize.  The amax pass's partial
+ * maxima go to a 4096-byte array that the library holds in device memory on
+ * each GPU it runs on (until the process ends); its address is looked up once
+ * per device, and the call itself allocates nothing.  Every call on one GPU
+ * shares that array and rewrites it completely before reading it, so calls
+ * that overlap on one GPU (concurrent streams) race and must not be issued;
+ * calls ordered on a stream, or across synchronised streams, are fine.
+ * Errors: those of nvfp4_quantize; EWORKSPACE if a call needs more than the
+ * array holds (none does at present: the partials are 4096 bytes for every
+ * shape); EHIP if the array's address cannot be looked up. */
+int nvfp4_quantize_noalloc(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                           int64_t ld_x, const float* amax, const nvfp4_tensor_t* out,
+                           void* stream);
 
 /* Transposed quantize: out = NVFP4 of X^T, i.e. output row k holds column k of
  * X [rows x cols] and the blocks of 16 run along X's rows.  This is the operand

@@ -60,6 +60,10 @@ def test_quantize_out_and_workspace():
         nv.nvfp4_quantize(x, out=_t(128, 64), workspace=torch.empty(8, dtype=torch.uint8))
     with pytest.raises(ValueError, match="amax"):
         nv.nvfp4_quantize(x, out=_t(128, 64), amax=torch.empty(1, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="codes"):
+        bad = _t(128, 64)
+        bad.codes = torch.empty(10, dtype=torch.uint8)
+        nv.nvfp4_quantize_noalloc(x, out=bad)
 
 
 def test_kv_outputs_and_page_list():

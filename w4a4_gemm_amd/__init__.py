@@ -21,7 +21,7 @@ __all__ = [
     "NVFP4Tensor", "KVCache", "LIB_PATH",
     "nvfp4_abi_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_kv_page_bytes",
     "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm_w4a4", "nvfp4_adaln_quantize",
-    "nvfp4_quantize_transposed",
+    "nvfp4_quantize_transposed", "nvfp4_quantize_noalloc",
     "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks", "nvfp4_kv_attention", "nvfp4_kv_window_pages",
     "SCALES_ROWMAJOR", "SCALES_TILED", "OP_QUANTIZE", "OP_KV_QUANTIZE", "OP_KV_ATTENTION",
     "OP_ADALN_QUANTIZE", "default_layout",
@@ -40,7 +40,7 @@ EXPORTS = (
     "nvfp4_abi_version", "nvfp4_status_string", "nvfp4_source_hash", "nvfp4_workspace_bytes",
     "nvfp4_kv_page_bytes",
     "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm_w4a4", "nvfp4_adaln_quantize",
-    "nvfp4_quantize_transposed",
+    "nvfp4_quantize_transposed", "nvfp4_quantize_noalloc",
     "nvfp4_kv_quantize", "nvfp4_kv_dequant_blocks", "nvfp4_kv_attention", "nvfp4_kv_window_pages",
 )
 
@@ -76,6 +76,8 @@ def _load():
         "nvfp4_kv_page_bytes": (i64, [i32, i32, i32]),
         "nvfp4_quantize": (ctypes.c_int, [vp, i32, i64, i64, i64, vp, ctypes.POINTER(_Tensor),
                                           vp, sz, vp]),
+        "nvfp4_quantize_noalloc": (ctypes.c_int, [vp, i32, i64, i64, i64, vp,
+                                                  ctypes.POINTER(_Tensor), vp]),
         "nvfp4_dequantize": (ctypes.c_int, [ctypes.POINTER(_Tensor), vp, i32, i64, vp]),
         "nvfp4_quantize_transposed": (ctypes.c_int, [vp, i32, i64, i64, i64, vp,
                                                      ctypes.POINTER(_Tensor), vp, sz, vp]),
@@ -240,6 +242,27 @@ def nvfp4_quantize(x, layout=None, amax=None, out=None, workspace=None, stream=N
                              _ptr(amax), ctypes.byref(cs), _ptr(workspace),
                              workspace.numel() if workspace is not None else 0, _stream(stream))
     _check(st, "nvfp4_quantize")
+    return out
+
+
+def nvfp4_quantize_noalloc(x, layout=None, amax=None, out=None, stream=None):
+    """nvfp4_quantize without a workspace: the library's per-device scratch array
+    holds the amax partials (calls that overlap on one GPU race).  ``out`` must be
+    given by callers that cannot allocate."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    rows, cols = x.shape
+    if layout is None:
+        layout = default_layout(rows, cols)
+    if out is None:
+        out = NVFP4Tensor(rows, cols, layout, device=x.device)
+    _check_nvfp4(out, "out", x.device)
+    if amax is not None:
+        _check_buffer(amax, "amax", torch.float32, x.device, numel=1)
+    cs = out.c()
+    st = _lib.nvfp4_quantize_noalloc(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0),
+                                     _ptr(amax), ctypes.byref(cs), _stream(stream))
+    _check(st, "nvfp4_quantize_noalloc")
     return out
 
 

@@ -1,6 +1,7 @@
 // C ABI of the NVFP4 library (declared in include/nvfp4.h): argument checks,
-// status codes and dispatch to the gfx950 kernels.  No allocation, no host
-// synchronisation, no library state.
+// status codes and dispatch to the gfx950 kernels.  No allocation and no host
+// synchronisation.  Library state: the per-device flags of launch.hpp and the
+// per-device address of the allocation-free quantize's scratch array.
 
 #include "nvfp4.h"
 #include <climits>
@@ -115,6 +116,23 @@ int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, i
   nvfp4::launch_quantize(x, x_dtype == NVFP4_BF16, rows, cols, ld_x, amax, out->codes,
                          out->scales, out->scale_layout == NVFP4_SCALES_TILED,
                          out->global_scale, workspace, as_stream(stream));
+  return finish();
+}
+
+int nvfp4_quantize_noalloc(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                           int64_t ld_x, const float* amax, const nvfp4_tensor_t* out,
+                           void* stream) {
+  const int st = check_quantize(x, x_dtype, rows, cols, ld_x, amax, out);
+  if (st) return st;
+  // the library's scratch array stands in for the workspace
+  const size_t need = nvfp4::quantize_workspace_bytes(rows, cols, amax != nullptr);
+  if (need > nvfp4::kQuantizeScratchBytes) return NVFP4_EWORKSPACE;
+  void* scratch = nullptr;
+  if (need && nvfp4::quantize_scratch(&scratch) != hipSuccess) return NVFP4_EHIP;
+  (void)hipGetLastError();
+  nvfp4::launch_quantize(x, x_dtype == NVFP4_BF16, rows, cols, ld_x, amax, out->codes,
+                         out->scales, out->scale_layout == NVFP4_SCALES_TILED,
+                         out->global_scale, scratch, as_stream(stream));
   return finish();
 }
 

@@ -38,6 +38,13 @@ void launch_quantize(const void* x, bool x_bf16, int64_t rows, int64_t cols, int
                      const float* amax, uint8_t* codes, uint8_t* scales, bool tiled,
                      float* gscale, void* workspace, hipStream_t stream);
 
+// Size of the file-scope device array that nvfp4_quantize_noalloc uses in
+// place of a workspace, and its address on the current device (looked up once
+// per device; no allocation).
+constexpr size_t kQuantizeScratchBytes = 4096;
+static_assert(kAmaxPartials * sizeof(float) <= kQuantizeScratchBytes, "scratch holds the partials");
+hipError_t quantize_scratch(void** ptr);
+
 void launch_dequantize(const uint8_t* codes, const uint8_t* scales, bool tiled,
                        const float* gscale, int64_t rows, int64_t cols, void* y, bool y_bf16,
                        int64_t ld_y, hipStream_t stream);

@@ -17,6 +17,9 @@
 // store 4 L contiguous bytes of a row), and the workgroup's rows lie inside one
 // 128-row band of the tiled scale layout.
 
+#include <mutex>
+#include <unordered_map>
+
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -720,6 +723,37 @@ void launch_quantize(const void* x, bool x_bf16, int64_t rows, int64_t cols, int
     else NVFP4_QLAUNCH(false, false);
   }
 #undef NVFP4_QLAUNCH
+}
+
+// ------------------------------------------------------------------ allocation-free scratch
+//
+// Device memory of nvfp4_quantize_noalloc: the amax partials live in this
+// file-scope array instead of a caller workspace.  Each device holds its own
+// copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, so its device address is looked up once per device (with that
+// device current) and only that address is handed to kernels.  Every call on
+// one device shares the array; the amax pass rewrites every partial before the
+// encode pass reads them, so nothing in it needs clearing between calls.
+static __device__ __align__(256) uint8_t scratch[kQuantizeScratchBytes];
+
+hipError_t quantize_scratch(void** ptr) {
+  static std::mutex mu;
+  static std::unordered_map<int, void*> addr;     // device -> address of `scratch`
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = addr.find(dev);
+  if (it != addr.end()) {
+    *ptr = it->second;
+    return hipSuccess;
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || p == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+  addr.emplace(dev, p);
+  *ptr = p;
+  return hipSuccess;
 }
 
 void launch_dequantize(const uint8_t* codes, const uint8_t* scales, bool tiled,
