@@ -118,30 +118,51 @@ def roofline_seconds(op):
 # ------------------------------------------------------------------ GPU step
 
 class Workload:
-    def __init__(self, dev):
+    """Device inputs and outputs of the step's ops; ``groups`` limits the build to
+    the ops being run (None: everything, as the full bench needs)."""
+
+    GROUPS = ("attn", "ffn", "kvw", "kvr", "adaln", "wgrad")
+    # op -> the input groups it needs
+    NEEDS = {"attn_quantize": ("attn",), "attn_gemm": ("attn",), "attn_dequantize": ("attn",),
+             "ffn_quantize": ("ffn",), "ffn_gemm1": ("ffn",), "ffn_requantize": ("ffn",),
+             "ffn_gemm2": ("ffn",), "kv_write": ("kvw",), "kv_read": ("kvr",),
+             "kv_attention": ("kvr",), "window_pages": ("kvr",), "adaln_quantize": ("adaln",),
+             "wgrad_quantize_t": ("ffn", "wgrad"), "wgrad_gemm": ("ffn", "wgrad")}
+
+    def __init__(self, dev, groups=None):
         import torch
         import synth
         import w4a4_gemm_amd as nv
-        self.nv, self.torch, self.dev = nv, torch, dev
+        self.nv, self.torch, self.dev, self.synth = nv, torch, dev, synth
+        groups = set(self.GROUPS if groups is None else groups)
+        for g in self.GROUPS:
+            if g in groups:
+                getattr(self, "_build_" + g)()
+        self._ops = self.ops() if groups >= {"attn", "ffn", "kvw", "kvr"} else None
+        torch.cuda.synchronize()
 
-        def bf16(bits):
-            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
-                torch.bfloat16).to(dev)
+    def _bf16(self, bits):
+        torch = self.torch
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).to(self.dev)
 
-        a = synth.attn_proj()
-        self.ax = bf16(a["x"])
-        self.aw = nv.nvfp4_quantize(bf16(a["w"]))                 # weights pre-quantized
+    def _build_attn(self):
+        nv, torch, dev = self.nv, self.torch, self.dev
+        a = self.synth.attn_proj()
+        self.ax = self._bf16(a["x"])
+        self.aw = nv.nvfp4_quantize(self._bf16(a["w"]))              # weights pre-quantized
         self.axq = nv.NVFP4Tensor(4096, 3072, nv.SCALES_TILED, device=dev)
         self.ay = torch.empty((4096, 3072), dtype=torch.bfloat16, device=dev)
         self.adq = torch.empty((4096, 3072), dtype=torch.bfloat16, device=dev)
         self.aws = torch.empty(nv.nvfp4_workspace_bytes(nv.OP_QUANTIZE, 4096, 3072, 0),
                                dtype=torch.uint8, device=dev)
-        del a
 
-        f = synth.ffn_pair()
-        self.fx = bf16(f["x"])
-        self.fw1 = nv.nvfp4_quantize(bf16(f["w1"]))
-        self.fw2 = nv.nvfp4_quantize(bf16(f["w2"]))
+    def _build_ffn(self):
+        nv, torch, dev = self.nv, self.torch, self.dev
+        f = self.synth.ffn_pair()
+        self.fx = self._bf16(f["x"])
+        self.fw1 = nv.nvfp4_quantize(self._bf16(f["w1"]))
+        self.fw2 = nv.nvfp4_quantize(self._bf16(f["w2"]))
         del f
         self.fxq = nv.NVFP4Tensor(8192, 3072, nv.SCALES_TILED, device=dev)
         self.fy1 = torch.empty((8192, 14336), dtype=torch.bfloat16, device=dev)
@@ -150,20 +171,28 @@ class Workload:
         self.famax = torch.zeros(1, dtype=torch.float32, device=dev)
         self.fws = torch.empty(nv.nvfp4_workspace_bytes(nv.OP_QUANTIZE, 8192, 3072, 0),
                                dtype=torch.uint8, device=dev)
+        # the requantize's input as the step produces it
+        nv.nvfp4_quantize(self.fx, out=self.fxq, workspace=self.fws)
+        nv.nvfp4_gemm_w4a4(self.fxq, self.fw1, out=self.fy1, y_amax=self.famax)
 
-        kb, vb = synth.kv_chunk()
-        self.kv_k, self.kv_v = bf16(kb), bf16(vb)
-        table = synth.page_permutation(28, 33)[None, :]
+    def _build_kvw(self):
+        nv, dev = self.nv, self.dev
+        kb, vb = self.synth.kv_chunk()
+        self.kv_k, self.kv_v = self._bf16(kb), self._bf16(vb)
+        table = self.synth.page_permutation(28, 33)[None, :]
         self.kv_w = nv.KVCache(1, 24, 128, 256, 28, 1, table, 28, device=dev)
         self.kv_ws = self.kv_w.workspace(7040)
 
-        r = synth.LongContextKV()
+    def _build_kvr(self):
+        nv, torch, dev = self.nv, self.torch, self.dev
+        r = self.synth.LongContextKV()
         self.lc = nv.KVCache(r.L, r.H, r.D, r.P, r.pages_per_layer, len(r.chunks), r.page_table,
                              r.n_phys, device=dev)
+        lc_ws = self.lc.workspace(max(n for _, n in r.chunks))
         for layer in range(r.L):
             for c in range(len(r.chunks)):
                 start, k, v = r.chunk_torch(layer, c, dev)
-                nv.nvfp4_kv_quantize(self.lc, layer, c, k, v, start, workspace=self.kv_ws)
+                nv.nvfp4_kv_quantize(self.lc, layer, c, k, v, start, workspace=lc_ws)
         self.lc_layers = r.L
         self.window = torch.tensor(r.window(), dtype=torch.int32, device=dev)
         n = self.window.numel() * r.P
@@ -171,17 +200,26 @@ class Workload:
         self.vh = torch.empty((n, r.H, r.D), dtype=torch.bfloat16, device=dev)
         # next row (not part of the step): one 880-token latent frame's queries
         # attending to layer 0's window, read straight from the NVFP4 pages
-        self.attn_q = bf16(synth.attn_queries(ATTN_QUERIES, r.H, r.D, seed=50))
+        self.attn_q = self._bf16(self.synth.attn_queries(ATTN_QUERIES, r.H, r.D, seed=50))
         self.attn_out = torch.empty_like(self.attn_q)
         self.attn_last = r.P
+        self.win_pages = torch.empty(256, dtype=torch.int32, device=dev)
+
+    def _build_adaln(self):
+        nv, torch, dev = self.nv, self.torch, self.dev
         # next row: the FFN input produced by LayerNorm + adaLN + NVFP4 in one kernel pair
-        d = synth.adaln_input(m=8192, k=3072, seed=72)
-        self.ln_x = bf16(d["x"])
+        d = self.synth.adaln_input(m=8192, k=3072, seed=72)
+        self.ln_x = self._bf16(d["x"])
         self.ln_shift = torch.from_numpy(d["shift"]).to(dev)
         self.ln_scale = torch.from_numpy(d["scale"]).to(dev)
         self.ln_rpg = d["rows_per_group"]
         self.ln_q = nv.NVFP4Tensor(8192, 3072, nv.SCALES_TILED, device=dev)
         self.ln_stats = torch.empty((8192, 2), dtype=torch.float32, device=dev)
+        self.ln_ws = torch.empty(nv.nvfp4_workspace_bytes(nv.OP_ADALN_QUANTIZE, 8192, 3072, 0),
+                                 dtype=torch.uint8, device=dev)
+
+    def _build_wgrad(self):
+        nv, torch, dev = self.nv, self.torch, self.dev
         # next row: wgrad of FFN GEMM1 on transposed-quantized operands
         gen = torch.Generator(device=dev).manual_seed(90)
         self.wg_dy = (torch.randn((8192, 14336), generator=gen, device=dev) * 1e-3).to(
@@ -192,11 +230,6 @@ class Workload:
         self.wg_ws = torch.empty(nv.nvfp4_workspace_bytes(nv.OP_QUANTIZE, 8192, 14336, 0),
                                  dtype=torch.uint8, device=dev)
         nv.nvfp4_quantize_transposed(self.wg_dy, out=self.wg_dyq, workspace=self.wg_ws)
-        self.win_pages = torch.empty(256, dtype=torch.int32, device=dev)
-        self.ln_ws = torch.empty(nv.nvfp4_workspace_bytes(nv.OP_ADALN_QUANTIZE, 8192, 3072, 0),
-                                 dtype=torch.uint8, device=dev)
-        self._ops = self.ops()
-        torch.cuda.synchronize()
 
     def ops(self):
         """The step's ops in order, as (name, callable) pairs."""
@@ -345,6 +378,7 @@ def cpu_baseline(ops):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = 1
+    host_cores = len(os.sched_getaffinity(0))
 
     # sample sizes chosen for roughly 10-30 s of oracle work on the host
     q_rows, g_rows, kv_tok, kv_pages = 2048, 512, 7040, 28
@@ -417,18 +451,34 @@ def cpu_baseline(ops):
         "value": 100.0 * roof / step,
         "unit": "% of MI355X roofline (whole step, extrapolated)",
         "cores": int(blas_threads),
+        "host_cores": host_cores,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"oracle timed on {q_rows}x3072 activation rows (quantize, bf16 dequantize), a "
                    f"{g_rows}x3072x3072 exact GEMM, a {kv_tok}-token KV chunk write and "
                    f"{kv_pages} KV pages read; "
                    "per-unit times scaled to the full step; elementwise numpy is single-"
-                   "threaded, the GEMM's fp64 BLAS uses the listed threads; the rows beside "
+                   "threaded, the GEMM's fp64 BLAS uses `cores` threads of the `host_cores` "
+                   "cores available to the process; the rows beside "
                    "the step: attention of 32 queries over those 28 pages, LayerNorm + adaLN + "
                    "NVFP4 of 256 x 3072, transposed quantize of 1024 x 3072, the exact GEMM's "
                    "per-FLOP time, and the whole window page list"),
         "step_seconds_estimate": step,
         "next_ops_seconds_estimate": nxt,
     }
+
+
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 # ------------------------------------------------------------------ measured traffic
@@ -457,7 +507,7 @@ def measured_traffic():
 
 def run_only(name, reps, warmup):
     import torch
-    wl = Workload(torch.device("cuda", 0))
+    wl = Workload(torch.device("cuda", 0), groups=Workload.NEEDS[name])
     fn = dict(wl.ops() + wl.next_ops())[name]
     for _ in range(warmup):
         fn()

@@ -120,11 +120,33 @@ def test_block_input_full_size_sampled_rows(m):
     x64 = F.bf16_bits_to_f64(x)
     mu, rstd, same = _check_stats(x64, stats.cpu().numpy(), 1e-6)
     assert same > 0.999
-    xp = A.modulate(x64, mu, rstd, shift.astype(np.float64), scale.astype(np.float64), rpg)
+    sh, sc = shift.astype(np.float64), scale.astype(np.float64)
+    xp = A.modulate(x64, mu, rstd, sh, sc, rpg)
     amax = float(np.max(np.abs(xp)))
+    # rows whose fp32 statistics differ from the oracle's (within the tolerance)
+    mu_ref, rstd_ref = A.row_stats(x64, 1e-6)
+    diff = np.nonzero((mu != mu_ref) | (rstd != rstd_ref))[0]
+    print(f"[adaln full size] {m} rows: {len(diff)} with statistics other than the oracle's",
+          flush=True)
     rows = np.sort(np.random.default_rng(84).choice(m, 96, replace=False))
-    rows = np.unique(np.concatenate([rows, [0, 879, 880, m - 1]]))   # group edges
+    rows = np.unique(np.concatenate([rows, [0, 879, 880, m - 1], diff]))  # group edges too
     want = Q.quantize(xp[rows], amax=amax)
     assert got.s_g == want.s_g
     assert np.array_equal(got.scales[rows], want.scales)
     assert np.array_equal(got.packed[rows], want.packed)
+    if len(diff):
+        # those rows against the oracle on its own statistics: x' moves by at most a
+        # few fp32 ulps, so a code may move only to a neighbouring E2M1 value where
+        # the two x' straddle a rounding boundary (same scale byte), and the scale
+        # byte only where the block maximum straddles an E4M3 boundary
+        xo = A.modulate(x64, mu_ref, rstd_ref, sh, sc, rpg)
+        own = Q.quantize(xo[diff], amax=float(np.max(np.abs(xo))))
+        if own.s_g != got.s_g:          # the tensor's largest |x'| sits in such a row
+            return
+        same_scale = np.repeat(got.scales[diff] == own.scales, 16, axis=1)
+        dg = Q.dequantize(Q.NVFP4(got.packed[diff], got.scales[diff], got.s_g), "f32")
+        do = Q.dequantize(own, "f32")
+        # one E2M1 step (at most 2) times s_b s_g, where the scale bytes agree
+        step = 2.0 * np.repeat(F.E4M3_GRID[got.scales[diff]], 16, axis=1) * got.s_g
+        assert np.all(np.abs(dg - do)[same_scale] <= step[same_scale])
+        assert np.mean(got.packed[diff] == own.packed) > 0.99

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import synth
-from helpers import bf16_tensor, dev, f32_tensor, from_oracle, to_oracle
+from helpers import assert_same_nvfp4, bf16_tensor, dev, f32_tensor, from_oracle, to_oracle
 from oracle import formats as F
 from oracle import nvfp4 as Q
 
@@ -256,3 +256,53 @@ def test_ffn_stage_parity():
     y2 = _run(want, w2q, torch.bfloat16)
     y2_ref, a2_ref = Q.gemm(want, w2q)
     assert Q.check_gemm_bf16(y2, y2_ref, a2_ref)[0]
+
+
+@pytest.mark.slow
+def test_ffn_chain_full_size_on_device():
+    """The FFN pair exactly as the benchmark runs it, every stage on the device's
+    own output: the 8192 x 3072 input quantize (bit-exact against the oracle over
+    the whole tensor), GEMM1 with the fused max|Y1|, the requantize of the stored
+    bf16 Y1 with that amax (bit-exact on four 128-row bands against the oracle's
+    quantize of the same stored rows, which with a given amax is row-local), and
+    GEMM2 on the device's NVFP4 Y1 (sampled outputs against exact dot products of
+    those bytes)."""
+    d = synth.ffn_pair()
+    x = bf16_tensor(d["x"])
+    xq = nv.NVFP4Tensor(8192, 3072, nv.SCALES_TILED, device=dev())
+    ws = torch.empty(nv.nvfp4_workspace_bytes(nv.OP_QUANTIZE, 8192, 3072, 0), dtype=torch.uint8,
+                     device=dev())
+    nv.nvfp4_quantize(x, out=xq, workspace=ws)
+    w1q = nv.nvfp4_quantize(bf16_tensor(d["w1"]))
+    w2q = nv.nvfp4_quantize(bf16_tensor(d["w2"]))
+    amax = torch.zeros(1, dtype=torch.float32, device=dev())
+    y1 = nv.nvfp4_gemm_w4a4(xq, w1q, torch.bfloat16, y_amax=amax)
+    y1q = nv.nvfp4_quantize(y1, layout=nv.SCALES_TILED, amax=amax)
+    y2 = nv.nvfp4_gemm_w4a4(y1q, w2q, torch.bfloat16)
+    torch.cuda.synchronize()
+    print("[ffn chain full size] device done", flush=True)
+
+    # stage 0: the input quantize, whole tensor
+    assert_same_nvfp4(to_oracle(xq), Q.quantize(F.bf16_bits_to_f64(d["x"])))
+    # the fused amax is max|Y1| as stored
+    y1_bits = y1.view(torch.int16).cpu().numpy().view(np.uint16)
+    am = float(amax.cpu()[0])
+    assert am == float(np.max(np.abs(F.bf16_bits_to_f64(y1_bits))))
+    # stage 2: requantize, bit-exact on 128-row bands (first, middle, last, random)
+    got = to_oracle(y1q)
+    assert got.s_g == Q.global_scale(am)
+    rng = np.random.default_rng(7)
+    for r0 in sorted({0, 4096, 8064, int(rng.integers(1, 63)) * 128}):
+        band = Q.quantize(F.bf16_bits_to_f64(y1_bits[r0:r0 + 128]), amax=am)
+        assert np.array_equal(got.scales[r0:r0 + 128], band.scales), f"scale bytes, band {r0}"
+        assert np.array_equal(got.packed[r0:r0 + 128], band.packed), f"codes, band {r0}"
+    # stage 3: GEMM2 on the device's NVFP4 Y1
+    w2o = to_oracle(w2q)
+    y = y2.float().cpu().numpy().astype(np.float64)
+    rows = rng.integers(0, 8192, 2048)
+    cols = rng.integers(0, 3072, 2048)
+    rows[:4] = [0, 0, 8191, 8191]
+    cols[:4] = [0, 3071, 0, 3071]
+    y_ref, a_ref = Q.gemm_pairs(got, w2o, rows, cols)
+    ok, n_clause, n_fail = Q.check_gemm_bf16(y[rows, cols], y_ref, a_ref)
+    assert ok, (n_clause, n_fail)

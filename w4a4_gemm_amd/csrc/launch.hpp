@@ -88,7 +88,7 @@ size_t kv_quantize_workspace_bytes(int64_t T, int64_t H, int64_t D);
 void launch_kv_quantize(const KvGeom& g, int32_t chunk_id, const uint16_t* k, const uint16_t* v,
                         int64_t T, int64_t start_token, void* workspace, hipStream_t stream);
 
-// Fused window attention (kv_attn.hip): head_dim 128, page_tokens % 64 == 0.
+// Fused window attention (kv_attn.hip): head_dim 64 or 128, page_tokens % 64 == 0.
 int attention_splits(int64_t n_q, int64_t n_heads, int64_t n_keys);
 size_t kv_attention_workspace_bytes(int64_t n_q, int64_t n_heads, int64_t n_keys);
 void launch_kv_attention(const KvGeom& g, const int32_t* logical_pages, int32_t n_pages,
