@@ -600,7 +600,7 @@ __device__ __forceinline__ void kv_flat_unit(const uint16_t* __restrict__ src,
 #pragma unroll
   for (int e = 0; e < 8; ++e) bm = fmaxf(bm, __builtin_fabsf(x[e]));
   bm = pair_max(bm);
-  const uint32_t sb = block_scale_byte(bm, te);
+  const uint32_t sb = block_scale_byte<kPre>(bm, te);
   const BlockEnc enc = make_block_enc(sb, te);
   if (kPre) {
 #pragma unroll

@@ -101,16 +101,26 @@ __device__ __forceinline__ TensorEnc make_tensor_enc(float s_g) {
 // b i6_hi (each product within 2^-24 of its exact value, the bracket 2^-19
 // wide).  gfx950's fp32 -> E4M3 conversion is RNE (checked on the device
 // against the exact rule for every fp32 in [0, 448]) and monotone, so equal
-// bytes for both ends are the byte of t; otherwise t lies within 2^-19 of an
-// E4M3 midpoint, or on one, and the exact fp64 path decides.  Clamping at 448
-// is exact: with saturation every t >= 448 gives 448.  Products below the
-// fp32 normal range are far below 2^-10 and give byte 0 either way.
+// bytes for both ends are the byte of t.  Otherwise t lies within 2^-19 of an
+// E4M3 midpoint, or on one, and the two bytes are neighbours (consecutive
+// midpoints are more than 6 % apart): the exact side of that midpoint Mid
+// decides.  6 Mid = 3 (E(lo) + E(hi)) has at most 7 significant bits, so one
+// fp32 FMA gives b - 6 Mid s_g with a single rounding; while s_g >= 2^-100
+// (no pre-scaling) that difference is a multiple of 2^-149 and so rounds to
+// zero only when it is zero, and its sign is exact.  With pre-scaling the fp64
+// path decides.  Clamping at 448 is exact: with saturation every t >= 448
+// gives 448.  Products below the fp32 normal range are far below 2^-10 and
+// give byte 0 either way.
+template <bool kPre>
 __device__ __forceinline__ uint32_t block_scale_byte(float b, const TensorEnc& t) {
   const float tl = fminf(b * t.i6_lo, 448.0f), th = fminf(b * t.i6_hi, 448.0f);
   const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(tl, th, 0, false);
   const uint32_t lo = pk & 0xFFu, hi = (pk >> 8) & 0xFFu;
   if (__builtin_expect(lo == hi, 1)) return lo;
-  return e4m3_block_scale(b, t.six_sg);
+  if (kPre) return e4m3_block_scale(b, t.six_sg);
+  const f32x2 e = __builtin_amdgcn_cvt_pk_f32_fp8((int)pk, false);   // E(lo), E(hi)
+  const float d = __builtin_fmaf(-3.0f * (e[0] + e[1]), t.s_g, b);
+  return (d > 0.0f || (d == 0.0f && (lo & 1u))) ? hi : lo;     // a tie goes to the even byte
 }
 
 // Per-block encoder.  Codes come from gfx950's fp32 -> E2M1 conversion (RNE,
@@ -137,8 +147,35 @@ __device__ __forceinline__ BlockEnc make_block_enc(uint32_t sb_byte, const Tenso
   return e;
 }
 
+// x[k] for k in 0..7: a select tree on the bits of k over register copies of
+// the values.  The empty asm makes each copy an opaque register value, so the
+// selects are not folded into a variable index into x (which would move x out
+// of registers).
+__device__ __forceinline__ float select8(const float* x, uint32_t k) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = x[i];
+    __asm__("" : "+v"(v[i]));
+  }
+  const bool b0 = (k & 1u) != 0, b1 = (k & 2u) != 0, b2 = (k & 4u) != 0;
+  const float a0 = b0 ? v[1] : v[0], a1 = b0 ? v[3] : v[2];
+  const float a2 = b0 ? v[5] : v[4], a3 = b0 ? v[7] : v[6];
+  const float c0 = b1 ? a1 : a0, c1 = b1 ? a3 : a2;
+  return b2 ? c1 : c0;
+}
+
 // Codes of 8 values (x already multiplied by `pre`) -> 8 nibbles, value j in
 // bits 4j+3..4j (so byte i holds values 2i, 2i+1 with the even one low).
+//
+// Where the two conversions disagree, hi's magnitude is lo's plus one: the
+// conversion is monotone, the products differ by less than 2^-18 relative, and
+// neighbouring E2M1 midpoints are at least a factor 1.4 apart.  The exact side
+// of the midpoint M between the two magnitudes then decides: M s_b has at most
+// 7 significant bits, so one FMA gives |x| - M s_b s_g with a single rounding
+// and an exact sign (zero only on a tie, which goes to the even magnitude).
+// Each pass of the loop settles one such nibble of the lane; lanes rarely have
+// more than one.
 __device__ __forceinline__ uint32_t encode8(const float* x, const BlockEnc& e,
                                             const TensorEnc& t) {
   uint32_t lo = 0, hi = 0;
@@ -150,21 +187,19 @@ __device__ __forceinline__ uint32_t encode8(const float* x, const BlockEnc& e,
   hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[4] * e.c_hi, x[5] * e.c_hi, 1.0f, 2);
   lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x[6] * e.c_lo, x[7] * e.c_lo, 1.0f, 3);
   hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[6] * e.c_hi, x[7] * e.c_hi, 1.0f, 3);
-  if (__builtin_expect(lo != hi, 0)) {
-    // resolve each differing nibble exactly
-    const float sg_pre = t.s_g * t.pre;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t cl = (lo >> (4 * j)) & 0xFu, ch = (hi >> (4 * j)) & 0xFu;
-      if (cl != ch) {
-        const uint32_t ml = cl & 7u;                     // magnitudes ml and ml + 1
-        const float mid = ml == 0 ? 0.25f : ml == 1 ? 0.75f : ml == 2 ? 1.25f
-                        : ml == 3 ? 1.75f : ml == 4 ? 2.5f : ml == 5 ? 3.5f : 5.0f;
-        const float d = __builtin_fmaf(-(mid * e.s_b), sg_pre, __builtin_fabsf(x[j]));
-        const bool up = d > 0.0f || (d == 0.0f && (ml & 1u));   // tie: to the even magnitude
-        lo = (lo & ~(0xFu << (4 * j))) | ((up ? ch : cl) << (4 * j));
-      }
-    }
+  uint32_t diff = lo ^ hi;
+  if (__builtin_expect(diff != 0u, 0)) {
+    const float hs = 0.5f * e.s_b;                    // exact
+    const float sg_pre = t.s_g * t.pre;               // exact
+    do {
+      const uint32_t sh = (uint32_t)__builtin_ctz(diff) & ~3u;     // bit offset of the nibble
+      const uint32_t ml = (lo >> sh) & 7u;                          // magnitude code of lo
+      const f32x2 q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ml | ((ml + 1u) << 4), 1.0f, 0);
+      const float ms = (q[0] + q[1]) * hs;                          // M s_b, exact
+      const float d = __builtin_fmaf(-ms, sg_pre, __builtin_fabsf(select8(x, sh >> 2)));
+      lo += (d > 0.0f || (d == 0.0f && (ml & 1u))) ? (1u << sh) : 0u;
+      diff &= ~(0xFu << sh);
+    } while (diff != 0u);
   }
   return lo;
 }
@@ -182,7 +217,7 @@ __device__ __forceinline__ void quantize_group(float* v, int nblk, const TensorE
       float bm = 0.0f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) bm = fmaxf(bm, __builtin_fabsf(v[16 * b + j]));
-      const uint32_t sb = block_scale_byte(bm, t);
+      const uint32_t sb = block_scale_byte<kPre>(bm, t);
       const BlockEnc enc = make_block_enc(sb, t);
       if (kPre) {
 #pragma unroll
@@ -326,10 +361,18 @@ __device__ __forceinline__ float pair_max(float v) {
   return fmaxf(v, __int_as_float(o));
 }
 
+// Max over the wave (every lane active; values >= 0): DPP within each row of 16
+// lanes, then the four row maxima.  The result is wave-uniform.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 }  // namespace nvfp4

@@ -183,7 +183,7 @@ __device__ __forceinline__ void quantize_tasks(const Raw8* raw, const TensorEnc&
 #pragma unroll
     for (int e = 0; e < 8; ++e) bm = fmaxf(bm, __builtin_fabsf(v[e]));
     bm = pair_max(bm);
-    const uint32_t sb = block_scale_byte(bm, te);
+    const uint32_t sb = block_scale_byte<kPre>(bm, te);
     const BlockEnc enc = make_block_enc(sb, te);
     if (kPre) {
 #pragma unroll
