@@ -49,11 +49,14 @@ GLOBAL_DIVISOR = 2688            # 6 * 448
 
 
 def global_scale(amax: float) -> float:
-    """s_g = RN32(amax / 2688); 1.0 when amax == 0 (reading)."""
+    """s_g = RN32(amax / 2688); 1.0 when amax == 0 (reading); 2^-149, the
+    smallest positive fp32, when a nonzero amax / 2688 rounds to zero (reading:
+    the pages define no block scale for s_g = 0)."""
     amax = float(amax)
     if amax == 0.0:
         return 1.0
-    return F.round_fraction_to_binary(Fraction(amax) / GLOBAL_DIVISOR, F.F32)
+    s = F.round_fraction_to_binary(Fraction(amax) / GLOBAL_DIVISOR, F.F32)
+    return s if s != 0.0 else 2.0 ** -149
 
 
 # --------------------------------------------------------------------------

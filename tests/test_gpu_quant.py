@@ -88,12 +88,25 @@ def test_all_zero_and_signed_zero():
     assert got.s_g == 1.0
 
 
-@pytest.mark.parametrize("scale", [2.0 ** -106, 2.0 ** -111, 2.0 ** 100])
+@pytest.mark.parametrize("scale", [2.0 ** -106, 2.0 ** -111, 2.0 ** -125, 2.0 ** -135,
+                                   2.0 ** -145, 2.0 ** 100])
 def test_extreme_tensor_scales(scale):
-    # s_g < 2^-100 takes the pre-scaled encoder; a huge scale stays in range too
+    # s_g < 2^-100 takes the pre-scaled encoder, down to subnormal s_g (2^-125 and
+    # below, where 1 / (6 s_g) is beyond the fp32 range) and to an amax whose
+    # quotient underflows (2^-145: s_g read as 2^-149); a huge scale stays in range too
     rng = np.random.default_rng(9)
     x = (rng.standard_normal((64, 128)) * scale).astype(np.float32)
-    _quantize_and_compare(x.astype(np.float64), f32_tensor(x), nv.SCALES_ROWMAJOR)
+    got = _quantize_and_compare(x.astype(np.float64), f32_tensor(x), nv.SCALES_ROWMAJOR)
+    if scale == 2.0 ** -145:
+        assert got.s_g == 2.0 ** -149
+
+
+@pytest.mark.parametrize("scale", [2.0 ** -125, 2.0 ** -135])
+def test_subnormal_bf16_tensor(scale):
+    rng = np.random.default_rng(19)
+    bits = synth.to_bf16_bits((rng.standard_normal((128, 256)) * scale).astype(np.float32))
+    x = synth.bf16_bits_to_f32(bits)
+    _quantize_and_compare(x.astype(np.float64), bf16_tensor(bits), nv.SCALES_TILED)
 
 
 def test_given_amax_path():

@@ -183,6 +183,22 @@ def test_global_scale_by_hand():
     assert Q.global_scale(1.0) == float(np.float32(1.0) / np.float32(2688.0))
 
 
+def test_global_scale_subnormal_and_underflow():
+    # 2688 * 2^-149 = 21 * 2^-142 is an fp32 subnormal and gives s_g = 2^-149 exactly
+    assert Q.global_scale(21.0 * 2.0 ** -142) == 2.0 ** -149
+    # 2^-140 / 2688 = 2^-147 / 21 is below half of 2^-149: RN32 gives 0, read as 2^-149
+    assert Q.global_scale(2.0 ** -140) == 2.0 ** -149
+    # a subnormal quotient that rounds normally: 2^-120 / 2688 = 2^-127 / 21, and
+    # 2^-127 / 21 = 2^-149 * (2^22 / 21) rounds to 199729 * 2^-149 (2^22 / 21 = 199728.76)
+    assert Q.global_scale(2.0 ** -120) == 199729 * 2.0 ** -149
+    # every block scale and code stays defined: the largest block of a tensor with that
+    # s_g takes byte 0x7E (448), exactly as for a normal s_g
+    x = np.zeros((1, 16))
+    x[0, 0] = 2.0 ** -140
+    q = Q.quantize(x)
+    assert q.s_g == 2.0 ** -149 and int(q.scales[0, 0]) <= 0x7E
+
+
 # ---------------------------------------------------------------- packing & layouts
 
 

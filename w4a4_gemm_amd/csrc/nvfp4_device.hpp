@@ -50,21 +50,26 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
 }
 
 // s_g = RN32(amax / 2688), or 1 when amax == 0.  __fdiv_rn is the correctly
-// rounded fp32 quotient.
+// rounded fp32 quotient.  A nonzero amax below 2688 * 2^-150 would give s_g =
+// 0, for which no block scale is defined; s_g is then the smallest positive
+// fp32, 2^-149.
 __device__ __forceinline__ float global_scale(float amax) {
-  return amax == 0.0f ? 1.0f : __fdiv_rn(amax, 2688.0f);
+  if (amax == 0.0f) return 1.0f;
+  const float q = __fdiv_rn(amax, 2688.0f);
+  return q == 0.0f ? 0x1p-149f : q;
 }
 
-// E4M3 byte nearest to the exact quotient t = b / (6 s_g) (ties to even,
-// saturating at 448).
+// E4M3 byte nearest to the exact quotient t = b / six (ties to even,
+// saturating at 448), with six = 6 s_g (times the tensor's pre-scaling, which
+// also multiplies b).
 //
-// t64 = RN64(b / (6 s_g)) is on the same side of every E4M3 midpoint as the
+// t64 = RN64(b / six) is on the same side of every E4M3 midpoint as the
 // exact t, and equals a midpoint only when t does: b has 24 significant bits
-// and 6 s_g M (M a midpoint, 5 bits) has at most 31, so a nonzero b - 6 s_g M
+// and six M (M a midpoint, 5 bits) has at most 31, so a nonzero b - six M
 // is at least 2^-33 relative, far above fp64's 2^-53 division error.  Rounding
 // t64 to 3 mantissa bits with RNE therefore gives the exact answer.
-__device__ __forceinline__ uint32_t e4m3_block_scale(float b, double six_sg) {
-  double t = (double)b / six_sg;
+__device__ __forceinline__ uint32_t e4m3_block_scale(float b, double six) {
+  double t = (double)b / six;
   if (t >= 464.0) return 0x7Eu;             // [448, 464] rounds to 448; beyond saturates
   if (t < 0x1p-6) {                         // subnormal range: m = RNE(t * 2^9) in 0..8
     return (uint32_t)__builtin_rint(t * 512.0);   // 8 is byte 0x08 = 2^-6
@@ -77,47 +82,51 @@ __device__ __forceinline__ uint32_t e4m3_block_scale(float b, double six_sg) {
 // ------------------------------------------------------------------ encoding
 
 // Per-tensor encoder constants.
-//   pre    1, or 2^64 when s_g < 2^-100: x is scaled up exactly so that the
-//          reciprocals below stay inside the fp32 range; it cancels in the codes.
-//   i6_lo, i6_hi  RN32(r (1 -/+ 2^-19)) with r = RN64(1 / (6 s_g)): they bracket
-//          1 / (6 s_g) from below and above by more than their rounding error.
+//   pre    1, or 2^64 when s_g < 2^-100: x (and a block's amax) is scaled up
+//          exactly so that every reciprocal below stays inside the fp32 range
+//          (s_g can be as small as 2^-149); it cancels in the codes and bytes.
+//   sg_pre s_g pre, exact, at least 2^-85.
+//   i6_lo, i6_hi  bracket R = 1 / (6 sg_pre) from below and above:
+//          r = rcp(RN32(6 sg_pre)) is within 2^-22.4 of R (one rounding of the
+//          product, one ulp of the reciprocal), and RN32(r (1 -/+ 2^-19))
+//          keeps each end more than 2^-19.2 away from R on its side.
 struct TensorEnc {
-  float s_g, pre, i6_lo, i6_hi;
-  double six_sg;                            // 6 s_g, exact in fp64
+  float s_g, pre, sg_pre, i6_lo, i6_hi;
 };
 
 __device__ __forceinline__ TensorEnc make_tensor_enc(float s_g) {
   TensorEnc t;
   t.s_g = s_g;
   t.pre = s_g < 0x1p-100f ? 0x1p64f : 1.0f;
-  t.six_sg = 6.0 * (double)s_g;
-  const double r = 1.0 / t.six_sg;
-  t.i6_lo = (float)(r * (1.0 - 0x1p-19));
-  t.i6_hi = (float)(r * (1.0 + 0x1p-19));
+  t.sg_pre = s_g * t.pre;
+  const float r = __builtin_amdgcn_rcpf(6.0f * t.sg_pre);
+  t.i6_lo = r * (1.0f - 0x1p-19f);
+  t.i6_hi = r * (1.0f + 0x1p-19f);
   return t;
 }
 
-// Block scale byte = E4M3 value nearest to t = b / (6 s_g).  b i6_lo < t <
-// b i6_hi (each product within 2^-24 of its exact value, the bracket 2^-19
-// wide).  gfx950's fp32 -> E4M3 conversion is RNE (checked on the device
-// against the exact rule for every fp32 in [0, 448]) and monotone, so equal
-// bytes for both ends are the byte of t.  Otherwise t lies within 2^-19 of an
-// E4M3 midpoint, or on one, and the two bytes are neighbours (consecutive
-// midpoints are more than 6 % apart): the exact side of that midpoint Mid
-// decides.  6 Mid = 3 (E(lo) + E(hi)) has at most 7 significant bits, so one
-// fp32 FMA gives b - 6 Mid s_g with a single rounding; while s_g >= 2^-100
-// (no pre-scaling) that difference is a multiple of 2^-149 and so rounds to
-// zero only when it is zero, and its sign is exact.  With pre-scaling the fp64
-// path decides.  Clamping at 448 is exact: with saturation every t >= 448
+// Block scale byte = E4M3 value nearest to t = b / (6 s_g) = b pre R.  b pre
+// i6_lo < t < b pre i6_hi (each product within 2^-24 of its exact value).
+// gfx950's fp32 -> E4M3 conversion is RNE (checked on the device against the
+// exact rule for every fp32 in [0, 448]) and monotone, so equal bytes for both
+// ends are the byte of t.  Otherwise t lies within about 2^-19 of an E4M3
+// midpoint, or on one, and the two bytes are neighbours (consecutive midpoints
+// are more than 6 % apart): the exact side of that midpoint Mid decides.
+// 6 Mid = 3 (E(lo) + E(hi)) has at most 7 significant bits, so one fp32 FMA
+// gives b - 6 Mid s_g with a single rounding; while s_g >= 2^-100 (no
+// pre-scaling) that difference is a multiple of 2^-149 and so rounds to zero
+// only when it is zero, and its sign is exact.  With pre-scaling the fp64
+// quotient decides.  Clamping at 448 is exact: with saturation every t >= 448
 // gives 448.  Products below the fp32 normal range are far below 2^-10 and
 // give byte 0 either way.
 template <bool kPre>
 __device__ __forceinline__ uint32_t block_scale_byte(float b, const TensorEnc& t) {
-  const float tl = fminf(b * t.i6_lo, 448.0f), th = fminf(b * t.i6_hi, 448.0f);
+  const float bp = kPre ? b * t.pre : b;                       // exact
+  const float tl = fminf(bp * t.i6_lo, 448.0f), th = fminf(bp * t.i6_hi, 448.0f);
   const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(tl, th, 0, false);
   const uint32_t lo = pk & 0xFFu, hi = (pk >> 8) & 0xFFu;
   if (__builtin_expect(lo == hi, 1)) return lo;
-  if (kPre) return e4m3_block_scale(b, t.six_sg);
+  if (kPre) return e4m3_block_scale(bp, 6.0 * (double)t.sg_pre);
   const f32x2 e = __builtin_amdgcn_cvt_pk_f32_fp8((int)pk, false);   // E(lo), E(hi)
   const float d = __builtin_fmaf(-3.0f * (e[0] + e[1]), t.s_g, b);
   return (d > 0.0f || (d == 0.0f && (lo & 1u))) ? hi : lo;     // a tie goes to the even byte
@@ -141,7 +150,7 @@ struct BlockEnc {
 __device__ __forceinline__ BlockEnc make_block_enc(uint32_t sb_byte, const TensorEnc& t) {
   BlockEnc e;
   e.s_b = e4m3_value(sb_byte);
-  const float r = __builtin_amdgcn_rcpf(e.s_b * (t.s_g * t.pre));
+  const float r = __builtin_amdgcn_rcpf(e.s_b * t.sg_pre);
   e.c_lo = sb_byte ? r * (1.0f - 0x1p-19f) : 0.0f;
   e.c_hi = sb_byte ? r * (1.0f + 0x1p-19f) : 0.0f;
   return e;
@@ -190,7 +199,7 @@ __device__ __forceinline__ uint32_t encode8(const float* x, const BlockEnc& e,
   uint32_t diff = lo ^ hi;
   if (__builtin_expect(diff != 0u, 0)) {
     const float hs = 0.5f * e.s_b;                    // exact
-    const float sg_pre = t.s_g * t.pre;               // exact
+    const float sg_pre = t.sg_pre;
     do {
       const uint32_t sh = (uint32_t)__builtin_ctz(diff) & ~3u;     // bit offset of the nibble
       const uint32_t ml = (lo >> sh) & 7u;                          // magnitude code of lo
