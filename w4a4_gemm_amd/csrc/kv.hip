@@ -568,20 +568,24 @@ __global__ __launch_bounds__(512) void kv_dequant_kernel(KvGeom g, int64_t n_phy
 
 // ------------------------------------------------------------------ launchers
 
-// Flat variant for head_dim dividing 512 (64, 128, 256): K and V are dense
-// [T][H][D], so lane u of the grid owns elements [8 u, 8 u + 8) -- one 16-byte
-// load per tensor, a wave reading 1 KB contiguous -- which is token
-// t = u / (H D / 8), head h, channels 8 j .. 8 j + 7 with j = u % (D / 8).  The
-// two lanes of a 16-value block exchange their maxima with one DPP swap (the
-// scheme of the activation quantize).  Whole waves stay in the loop (lanes past
-// the end take the last unit and store nothing) so the swap always has both
-// lanes; the loop strides over the grid.
+// Flat variant for head_dim dividing 512 (64, 128, 256).  A row is one
+// (head, token) pair, taken head-major (row r = h T + t); lane u of the grid
+// owns channels 8 j .. 8 j + 7 (j = u % (D / 8)) of row u / (D / 8): one
+// 16-byte load per tensor.  A workgroup thus covers consecutive tokens of one
+// head, whose page rows are consecutive too: it writes whole runs of codes and
+// of scale bytes (16 tokens x 8 bytes = 128 bytes of scales for head_dim 128)
+// instead of leaving neighbouring tokens' scale bytes to workgroups on other
+// XCDs, whose L2s would each write back a partial span.  The two lanes of a
+// 16-value block exchange their maxima with one DPP swap (the scheme of the
+// activation quantize).  Whole waves stay in the loop (lanes past the end take
+// the last unit and store nothing) so the swap always has both lanes; the
+// loop strides over the grid.
 template <int kD, bool kPre>
 __device__ __forceinline__ void kv_flat_unit(const uint16_t* __restrict__ src,
-                                             const float* __restrict__ mu, int64_t u,
+                                             const float* __restrict__ mu, uint32_t e0,
                                              const TensorEnc& te, bool store, uint8_t* cp,
                                              uint8_t* sp, int j) {
-  const u32x4 w = *(const u32x4*)(src + 8 * u);
+  const u32x4 w = *(const u32x4*)(src + e0);
   float x[8];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -613,11 +617,12 @@ __device__ __forceinline__ void kv_flat_unit(const uint16_t* __restrict__ src,
   }
 }
 
+// p_shift: log2(page_tokens) when that is a power of two, else -1 (divide).
 template <int kD>
 __global__ __launch_bounds__(256) void kv_quantize_flat_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t T,
     int64_t start_token, int32_t chunk_id, KvWorkspace ws, int n_fin_wg,
-    KvGeom g, int64_t n_phys, const float* __restrict__ mu_chunk) {
+    KvGeom g, int64_t n_phys, const float* __restrict__ mu_chunk, int p_shift) {
   const float s_gk = global_scale(max_of(ws.kamax, n_fin_wg));
   const float s_gv = global_scale(max_of(ws.vamax_f, n_fin_wg));
   const TensorEnc tk = make_tensor_enc(s_gk), tv = make_tensor_enc(s_gv);
@@ -625,21 +630,23 @@ __global__ __launch_bounds__(256) void kv_quantize_flat_kernel(
     g.k_gscale[chunk_id] = s_gk;
     g.v_gscale[chunk_id] = s_gv;
   }
-  // 32-bit indices (the launcher checks T H D / 8 and start_token + T < 2^31).
-  // The grid stride is a whole number of rows, so a lane's (token, head) moves
-  // by a fixed step each iteration and its channel chunk j never changes.
-  constexpr uint32_t kLpr = kD / 8;                     // lanes per (token, head) row
-  const uint32_t H = g.n_heads, P = g.page_tokens;
-  const uint32_t n = (uint32_t)T * H * kLpr;
+  // 32-bit indices (the launcher checks T H D and start_token + T < 2^31, and
+  // page_bytes < 2^32; T >= 1).  The grid stride is a whole number of rows, so a
+  // lane's (head, token) moves by a fixed step each iteration and its channel
+  // chunk j never changes.
+  constexpr uint32_t kLpr = kD / 8;                     // lanes per row
+  const uint32_t H = g.n_heads, P = g.page_tokens, Tu = (uint32_t)T;
+  const uint32_t n = Tu * H * kLpr;
   const uint32_t codes_region = H * P * (kD / 2);
   const uint32_t scales_region = H * P * (kD / 16);
   const uint32_t stride = gridDim.x * 256u;
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t u0 = blockIdx.x * 256u + threadIdx.x;
   const uint32_t j = u0 % kLpr;
-  const uint32_t dr = stride / kLpr, dt = dr / H, dh = dr % H;
+  const uint32_t dr = stride / kLpr, dh = dr / Tu, dt = dr % Tu;
   uint32_t r0 = u0 / kLpr;
-  uint32_t t = r0 / H, h = r0 % H;
+  uint32_t h = r0 / Tu, t = r0 % Tu;
+  const uint32_t rs = H * kD;                           // elements per token of K and V
   const float* mu = mu_chunk + 8 * j;
   // the encoders' pre-scaling is uniform per tensor: pick it outside the loop so
   // the loop body has no branch between the K and V loads
@@ -648,10 +655,10 @@ __global__ __launch_bounds__(256) void kv_quantize_flat_kernel(
     for (uint32_t base = blockIdx.x * 256u + (threadIdx.x - lane); base < n; base += stride) {
       const uint32_t u = base + lane;
       const bool in = u < n;
-      const uint32_t tc = in ? t : (uint32_t)T - 1;     // lanes past the end: valid addresses
-      const uint32_t uc = in ? u : n - 1;
+      const uint32_t tc = in ? t : Tu - 1;              // lanes past the end: valid addresses
+      const uint32_t hc = in ? h : H - 1;
       const uint32_t pos = (uint32_t)start_token + tc;
-      const uint32_t lp = pos / P;
+      const uint32_t lp = p_shift >= 0 ? pos >> p_shift : pos / P;
       const uint32_t slot = pos - lp * P;
       // page -> chunk bookkeeping (one lane per touched page)
       if (in && h == 0 && j == 0) {
@@ -667,19 +674,20 @@ __global__ __launch_bounds__(256) void kv_quantize_flat_kernel(
       const int64_t phys = g.page_table[lp];
       const bool store = in && phys >= 0 && phys < n_phys;
       uint8_t* page = g.pool + (store ? phys : 0) * g.page_bytes;
-      const uint32_t row = h * P + slot;
+      const uint32_t row = hc * P + slot;
       uint8_t* kc = page + (row * (kD / 2) + 4 * j);
       uint8_t* ks = page + (codes_region + row * (kD / 16) + (j >> 1));
       uint8_t* vc = page + (codes_region + scales_region + row * (kD / 2) + 4 * j);
       uint8_t* vs = page + (2 * codes_region + scales_region + row * (kD / 16) + (j >> 1));
-      kv_flat_unit<kD, kPk>(k, mu + h * kD, uc, tk, store, kc, ks, j);
-      kv_flat_unit<kD, kPv>(v, nullptr, uc, tv, store, vc, vs, j);
-      // next iteration's (token, head)
-      h += dh;
+      const uint32_t e0 = tc * rs + hc * kD + 8 * j;    // first element of the lane's 8
+      kv_flat_unit<kD, kPk>(k, mu + hc * kD, e0, tk, store, kc, ks, j);
+      kv_flat_unit<kD, kPv>(v, nullptr, e0, tv, store, vc, vs, j);
+      // next iteration's (head, token)
       t += dt;
-      if (h >= H) {
-        h -= H;
-        t += 1;
+      h += dh;
+      if (t >= Tu) {
+        t -= Tu;
+        h += 1;
       }
     }
   };
@@ -705,7 +713,7 @@ void launch_kv_quantize(const KvGeom& g, int32_t chunk_id, const uint16_t* k, co
   hipLaunchKernelGGL(kv_finalize_kernel, dim3(nfw), dim3(kFinalizeThreads), 0, stream, ws, T, C,
                      nsw, mu);
   const int D = g.head_dim;
-  const bool small = T * g.n_heads * (D / 8) < (int64_t(1) << 31) &&
+  const bool small = T * g.n_heads * D < (int64_t(1) << 31) &&
                      start_token + T < (int64_t(1) << 31) &&
                      g.page_bytes < (int64_t(1) << 32);
   if ((D == 64 || D == 128 || D == 256) && small) {
@@ -715,9 +723,11 @@ void launch_kv_quantize(const KvGeom& g, int32_t chunk_id, const uint16_t* k, co
     // 7040-token chunk than 8192 short workgroups (too few waves stay resident)
     int64_t wgs = (lanes + 255) / 256;
     wgs = wgs < 2048 ? wgs : 2048;
+    const int P = g.page_tokens;
+    const int p_shift = (P & (P - 1)) == 0 ? __builtin_ctz((unsigned)P) : -1;
     const auto go = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(256), 0, stream, k, v, T, start_token,
-                         chunk_id, ws, nfw, g, g.n_phys_pages, (const float*)mu);
+                         chunk_id, ws, nfw, g, g.n_phys_pages, (const float*)mu, p_shift);
     };
     if (D == 64) go(kv_quantize_flat_kernel<64>);
     else if (D == 128) go(kv_quantize_flat_kernel<128>);
