@@ -46,6 +46,12 @@ COMMON = [
 ]
 
 
+# Flags of single sources.  kv_attn.hip: the attention's logits and weights are
+# finite, and without NaNs to honour the compiler takes a float max in one
+# instruction instead of first canonicalizing both operands.
+SOURCE_FLAGS = {"kv_attn.hip": ["-fno-honor-nans"]}
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -76,7 +82,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        extra = tag if src == "capi.cpp" else []
+        extra = (tag if src == "capi.cpp" else []) + SOURCE_FLAGS.get(src, [])
         cmds.append([HIPCC, *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:

@@ -7,14 +7,19 @@
 // s_gK + mu), V^ = RN_bf16(q s_b s_gV)) and consumed at once by a
 // flash-attention step, so no bf16 K or V reaches HBM.
 //
-// Layout of work: a workgroup is one head and 128 queries (4 waves x 32).
-// Each wave computes the transposed products on the bf16 MFMA
+// Layout of work: a workgroup is one head and 256 queries (8 waves x 32, two
+// waves per SIMD), so each decoded block serves 256 queries; a wave keeps its
+// 32 query rows in registers.  K^ and V^T are double-buffered in LDS: while
+// the waves multiply block b from one buffer, the workgroup decodes block
+// b + 1 into the other (the decode's VALU work issues under the MFMAs), so a
+// block costs one barrier.  Each wave computes the transposed products on the
+// bf16 MFMA
 //   S^T = K^ Q^T    (32 keys x 32 queries per v_mfma_f32_32x32x16_bf16 tile)
 //   O^T += V^T P^T  (32 channels x 32 queries per tile)
 // so that in both accumulators a lane owns one query (column lane % 32) and
 // its registers run over keys or channels.  The online softmax (running max
 // m, running sum l, rescaling of O) is then per lane plus one exchange with
-// lane ^ 32, and P goes from the S^T registers straight into the second
+// lane ^ 32 (a permlane swap), and P goes from the S^T registers straight into the second
 // MFMA: the MFMA sums over its 16 k values in any order, so the k order of
 // a step is taken to be the key order of the S^T registers, and V^T is read
 // from LDS in that same order.  Logits are scaled by scale * log2(e) and
@@ -33,7 +38,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 #ifndef NVFP4_ATTN_WAVES
-#define NVFP4_ATTN_WAVES 4
+#define NVFP4_ATTN_WAVES 8
 #endif
 constexpr int kWaves = NVFP4_ATTN_WAVES;  // waves per workgroup, 32 queries each
 constexpr int kThreads = 64 * kWaves;
@@ -47,24 +52,49 @@ template <int kD>
 struct Shape {
   static constexpr int kGroups = kD / 8;                 // 8-channel units per key
   static constexpr int kKPT = kKB * kGroups / kThreads;  // keys per thread in a block's decode
-  static constexpr int kKsRow = kD + 8;                  // bf16 per Q / K^ row in LDS (conflict-free)
-  static constexpr size_t kLds =                         // Q rows + K^ rows + V^T rows + K means
-      2 * ((size_t)kQB * kKsRow + (size_t)kKB * kKsRow + (size_t)kD * kVtRow) + 2 * kD * 4;
-  static_assert(kKPT == 2 || kKPT == 4, "a thread decodes 2 or 4 keys of a block");
-  static_assert(kThreads >= 2 * kD && kThreads == 2 * kQB, "thread roles of the Q and mean loads");
+  static constexpr int kKsRow = kD + 8;                  // bf16 per K^ row in LDS (conflict-free)
+  static constexpr size_t kKsElems = (size_t)kKB * kKsRow;   // bf16 per K^ buffer
+  static constexpr size_t kVtElems = (size_t)kD * kVtRow;    // bf16 per V^T buffer
+  static constexpr size_t kLds =                         // 2 x (K^ rows + V^T rows + K means)
+      2 * (2 * (kKsElems + kVtElems) + 2 * kD * 4);
+  static_assert(kKPT == 1 || kKPT == 2 || kKPT == 4, "a thread decodes 1, 2 or 4 keys of a block");
+  static_assert(kThreads >= 2 * kD, "one thread per K mean of the page's two chunks");
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// x combined with the x of lane ^ 32, without LDS: gfx950's permlane32 swap
+// exchanges the upper half of one copy with the lower half of another, so
+// lane i of the two results holds x of lanes i % 32 and i % 32 + 32 (in some
+// order); max and + of the two are symmetric in that order.
+__device__ __forceinline__ float max_lane32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_lane32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Position of key k (0..63) in a V^T row: bits 2 and 3 of k swapped.  The
+// O^T MFMA's lane half `half` takes, in step kk of key tile kt, the keys
+// 32 kt + 16 kk + 4 half + {0..3} and the same plus 8; with this order they
+// are the 8 contiguous positions 32 kt + 16 kk + 8 half .. (one 16-byte read).
+__device__ __forceinline__ int vt_pos(int k) {
+  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
 // Per-page facts, uniform over the workgroup.
+// (32-bit fields only: a struct with padding bytes is copied through scratch
+// memory when the pipeline rotates it.)
 struct PageInfo {
   const uint8_t* page;    // a valid page address (page 0 when unmapped: loads stay in bounds)
-  bool mapped;
+  int mapped;
   int valid;              // valid slots of the page (keys beyond are masked)
   int split;              // slots [0, split) belong to chunk c0, the rest to c1
   int c0, c1;
   float sgk0, sgk1, sgv0, sgv1;
-  bool vcheck;            // a V^ product of this page may need the bf16 midpoint fix-up
+  int vcheck;             // a V^ product of this page may need the bf16 midpoint fix-up
 };
 
 __device__ __forceinline__ PageInfo page_info(const KvGeom& g, int64_t n_phys,
@@ -171,18 +201,24 @@ __device__ __forceinline__ void decode_block(const PageInfo& p, int s0, int cs,
 #pragma unroll
     for (int e = 0; e < 4; ++e) vw[i][e] = vo[e];
   }
-  // V^T row 8 sub + c holds channel c of the 4 keys: bf16 of key i is the
-  // low (c even) or high (c odd) half of vw[i][c / 2]
-  const int k0 = kKPT * (threadIdx.x / kGroups);
+  // V^T row 8 sub + c holds channel c of the keys: bf16 of key i is the low
+  // (c even) or high (c odd) half of vw[i][c / 2].  Keys sit at position
+  // vt_pos(key) of the row (runs of 4 keys stay contiguous).
+  const int k0 = vt_pos(kKPT * (threadIdx.x / kGroups));
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
+    uint16_t* vt = Vt + (8 * sub + c) * kVtRow + k0;
+    if (kKPT == 1) {
+      *vt = (uint16_t)((c & 1) ? vw[0][c >> 1] >> 16 : vw[0][c >> 1]);
+      continue;
+    }
     const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-    const uint32_t lo = __builtin_amdgcn_perm(vw[1][c >> 1], vw[0][c >> 1], sel);
+    const uint32_t lo = __builtin_amdgcn_perm(vw[kKPT > 1 ? 1 : 0][c >> 1], vw[0][c >> 1], sel);
     if (kKPT == 4) {
       const uint32_t hi = __builtin_amdgcn_perm(vw[kKPT - 1][c >> 1], vw[kKPT - 2][c >> 1], sel);
-      *(u32x2*)(Vt + (8 * sub + c) * kVtRow + k0) = u32x2{lo, hi};
+      *(u32x2*)vt = u32x2{lo, hi};
     } else {
-      *(uint32_t*)(Vt + (8 * sub + c) * kVtRow + k0) = lo;
+      *(uint32_t*)vt = lo;
     }
   }
 }
@@ -196,11 +232,11 @@ __device__ __forceinline__ void decode_block(const PageInfo& p, int s0, int cs,
 int attention_splits(int64_t n_q, int64_t n_heads, int64_t n_keys) {
   const int64_t base = ((n_q + kQB - 1) / kQB) * n_heads;
   const int64_t blocks = (n_keys + kKB - 1) / kKB;
-  if (base >= 512 || blocks < 16) return 1;
-  // Workgroups run two per CU (512 at once on 256 CUs).  Time ~ rounds of
+  // Two waves per SIMD: 8 / kWaves workgroups per CU run at once.  Time ~ rounds of
   // workgroups x blocks per workgroup, plus the merge, which reads every split's
   // partial O (about 0.6 block-times per split here); each split keeps >= 8 blocks.
-  constexpr int64_t kSlots = 512;
+  constexpr int64_t kSlots = 256 * (8 / kWaves);
+  if (base >= kSlots || blocks < 16) return 1;
   const int64_t s_max = blocks / 8 < 64 ? blocks / 8 : 64;
   int64_t best_s = 1;
   double best = (double)blocks * ((base + kSlots - 1) / kSlots);
@@ -221,13 +257,140 @@ size_t kv_attention_workspace_bytes(int64_t n_q, int64_t n_heads, int64_t n_keys
   return (size_t)s * n_q * n_heads * (kMaxD + 2) * sizeof(float);
 }
 
+// One block of keys for a wave's 32 queries: S^T = K^ Q^T from buffer (Kc, Vc),
+// the online-softmax update of (m, l, O), and O^T += V^T P^T.  `decode_next`
+// runs between the S^T MFMAs and the softmax: it decodes the next block into
+// the other buffer (restrict-qualified, so its LDS stores may pass these
+// reads and its VALU work can issue under the MFMAs).
+template <int kD, typename Decode>
+__device__ __forceinline__ void attend_block(const uint16_t* __restrict__ Kc,
+                                             const uint16_t* __restrict__ Vc,
+                                             const bf16x8 (&qr)[kD / 16], int lane, int s0,
+                                             int valid, float scale_log2e, float& m, float& l,
+                                             f32x16 (&o)[kD / 32], const Decode& decode_next) {
+  constexpr int kKsRow = Shape<kD>::kKsRow;
+  const int half = lane >> 5;
+  // S^T tiles: keys 32 kt + (r / 4) * 8 + 4 half + r % 4 of this block, query lane % 32
+  // (the two key tiles' MFMA chains alternate, sharing each Q fragment)
+  f32x16 st[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[kt][r] = 0.0f;
+  {
+    const uint16_t* kp = Kc + (lane & 31) * kKsRow + 8 * half;
+#pragma unroll
+    for (int s = 0; s < kD / 16; ++s) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(*(const u32x4*)(kp + 32 * kt * kKsRow + 16 * s)), qr[s], st[kt], 0, 0, 0);
+    }
+  }
+  decode_next();
+  // online softmax for this lane's query (keys split between lane and lane ^ 32),
+  // in log2 units: t = S c with c = |scale| log2(e) >= 0, so the block max of t is
+  // RN(c max S) and each weight is exp2(fma(S, c, -m)).  Keys past the last
+  // valid slot only occur in a block that is not full: a full block (the
+  // usual case, a uniform test) takes a loop without per-key masks.  (This
+  // file is compiled without NaN support, so fmaxf is one instruction.)
+  const bool full = s0 + kKB <= valid;
+  float mb = -__builtin_inff();
+  if (full) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mb = fmaxf(mb, st[kt][r]);
+  } else {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kt + (r >> 2) * 8 + 4 * half + (r & 3);
+        if (s0 + key < valid) mb = fmaxf(mb, st[kt][r]);
+      }
+  }
+  mb = max_lane32(mb);
+  const float m_new = fmaxf(m, mb * scale_log2e);          // finite: the block has a valid key
+  const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first block
+  float ps = 0.0f;
+  if (full) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kt][r], scale_log2e, -m_new));
+        st[kt][r] = p;
+        ps += p;
+      }
+  } else {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kt + (r >> 2) * 8 + 4 * half + (r & 3);
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kt][r], scale_log2e, -m_new));
+        if (s0 + key >= valid) p = 0.0f;
+        st[kt][r] = p;
+        ps += p;
+      }
+  }
+  ps = sum_lane32(ps);
+  l = l * alpha + ps;
+  m = m_new;
+  if (__any(alpha != 1.0f)) {                             // the running max moved
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+  }
+
+  // O^T += V^T P^T.  Step kk of key tile kt: k index j of lane half `half` is
+  // key 32 kt + 16 kk + (j / 4) * 8 + 4 half + j % 4 = S^T register 8 kk + j.
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 pb;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pb[j] = pack_bf16x2(st[kt][8 * kk + 2 * j], st[kt][8 * kk + 2 * j + 1]);
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt) {
+        // the 8 keys of this lane half are contiguous in the V^T row (vt_pos)
+        const uint16_t* vp = Vc + (32 * dt + (lane & 31)) * kVtRow + 32 * kt + 16 * kk + 8 * half;
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*(const u32x4*)vp),
+                                                        as_bf16x8(pb), o[dt], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Decode block (page facts p, first slot s0, raw inputs r) into (Kn, Vn) with
+// the K means in Mu.
+template <int kD>
+__device__ __forceinline__ void decode_any(const PageInfo& p, int s0,
+                                           const BlockRaw<Shape<kD>::kKPT>& r,
+                                           const float* __restrict__ Mu,
+                                           uint16_t* __restrict__ Kn, uint16_t* __restrict__ Vn) {
+  const bool one_chunk = s0 + kKB <= p.split || s0 >= p.split;
+  const bool simple = p.mapped && s0 + kKB <= p.valid && one_chunk;
+  const int cs = s0 >= p.split ? 1 : 0;
+  if (simple) {
+    if (p.vcheck) decode_block<kD, true, true>(p, s0, cs, r, Mu, Kn, Vn);
+    else decode_block<kD, false, true>(p, s0, cs, r, Mu, Kn, Vn);
+  } else {
+    if (p.vcheck) decode_block<kD, true, false>(p, s0, 0, r, Mu, Kn, Vn);
+    else decode_block<kD, false, false>(p, s0, 0, r, Mu, Kn, Vn);
+  }
+}
+
 // Split `split` of `n_split` handles key blocks [b0, b1) of the window.  With
 // one split the result is normalized and written as bf16; otherwise the
 // unnormalized fp32 O^T, the running max m (log2 units) and the sum l go to
 // the workspace: O at part + ((split * n_q + n) * H + h) * D, (m, l) after all
 // O values.
-// Two workgroups per CU (registers capped at 256 per lane), so one
-// workgroup's decode overlaps the other's MFMAs.
+// Two waves per SIMD (registers capped at 256 per lane): one wave's softmax
+// and decode overlap the other's MFMAs.
 template <int kD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void kv_attention_kernel(KvGeom g, int64_t n_phys,
                                                            const int32_t* __restrict__ pages,
@@ -237,34 +400,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                                                            uint32_t q_sign,
                                                            uint16_t* __restrict__ out,
                                                            float* __restrict__ part, int n_split) {
-  // LDS (Shape<kD>::kLds bytes, dynamic): Q rows, K^ rows, V^T rows, K means of chunk c0 then c1
+  // LDS (Shape<kD>::kLds bytes, dynamic): K^ rows, V^T rows, K means of chunk c0 then c1
   constexpr int kKsRow = Shape<kD>::kKsRow;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t* Qs = smem;
-  uint16_t* Ks = Qs + kQB * kKsRow;
-  uint16_t* Vt = Ks + kKB * kKsRow;
-  float* Mu = (float*)(Vt + kD * kVtRow);
+  constexpr size_t kKsElems = Shape<kD>::kKsElems, kVtElems = Shape<kD>::kVtElems;
+  uint16_t* Kb = smem;                                    // buffer i at Kb + i kKsElems
+  uint16_t* Vb = Kb + 2 * kKsElems;                       // buffer i at Vb + i kVtElems
+  float* Mb = (float*)(Vb + 2 * kVtElems);                // buffer i at Mb + i 2 kD
   const int H = g.n_heads, P = g.page_tokens;
   const int h = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5;
   const int64_t qrow = (int64_t)blockIdx.x * kQB + wave * 32 + (lane & 31);
 
-  // The workgroup's 128 query rows go to LDS once (two threads per row, kD / 2
-  // channels each); the first barrier of the block loop publishes them.  They
-  // are the B operand of S^T = K^ Q^T: step s covers channels 16 s .. 16 s + 15,
-  // lane half `half` the 8 channels 16 s + 8 half ..
+  // The lane's query row in registers, as the B operand of S^T = K^ Q^T:
+  // step s covers channels 16 s .. 16 s + 15, lane half `half` the 8 channels
+  // 16 s + 8 half ..
+  bf16x8 qr[kD / 16];
   {
-    const int row = tid >> 1;
-    const int64_t qr = (int64_t)blockIdx.x * kQB + row;
-    const uint16_t* qp = q + ((qr < n_q ? qr : n_q - 1) * H + h) * kD + (kD / 2) * (tid & 1);
-    uint16_t* qs = Qs + row * kKsRow + (kD / 2) * (tid & 1);
+    const uint16_t* qp = q + ((qrow < n_q ? qrow : n_q - 1) * H + h) * kD + 8 * half;
 #pragma unroll
-    for (int i = 0; i < kD / 16; ++i) {
-      u32x4 v = *(const u32x4*)(qp + 8 * i);
+    for (int s = 0; s < kD / 16; ++s) {
+      u32x4 v = *(const u32x4*)(qp + 16 * s);
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] ^= q_sign;           // -q when the scale is negative
-      *(u32x4*)(qs + 8 * i) = v;
+      qr[s] = as_bf16x8(v);
     }
   }
   f32x16 o[kD / 32];
@@ -278,112 +438,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int nb = n_pages * bpp;
   const int b0 = (int)((int64_t)nb * split / n_split), b1 = (int)((int64_t)nb * (split + 1) / n_split);
 
-  // software pipeline: the raw inputs of block b + 1 are in flight while
-  // block b is decoded and consumed
-  PageInfo pn;
-  BlockRaw<Shape<kD>::kKPT> rn;
+  // Pipeline: on entry to iteration b, buffer b & 1 holds decoded block b, the
+  // raw inputs of block b + 1 are in flight (rn) and Mu buffer (b + 1) & 1
+  // holds its K means.  Iteration b multiplies block b and, between its S^T
+  // MFMAs and its softmax, decodes block b + 1 and then reuses rn to fetch
+  // block b + 2; one barrier ends it.
   if (b0 < b1) {
-    pn = page_info(g, n_phys, pages, b0 / bpp, n_pages, last_tokens);
-    fetch_block<kD>(g, pn, h, (b0 % bpp) * kKB, rn);
-  }
-  for (int b = b0; b < b1; ++b) {
-    const int s0 = (b % bpp) * kKB;
-    const PageInfo pc = pn;
-    const BlockRaw<Shape<kD>::kKPT> rc = rn;
-    if (b + 1 < b1) {
-      if ((b + 1) % bpp == 0) pn = page_info(g, n_phys, pages, (b + 1) / bpp, n_pages, last_tokens);
-      fetch_block<kD>(g, pn, h, ((b + 1) % bpp) * kKB, rn);
-    }
-    if (pc.valid <= s0) continue;                           // whole block masked (uniform)
-    if (tid < 2 * kD) Mu[tid] = rc.mu;     // safe: the previous decode's reads of Mu
-    __syncthreads();                       // finished before the previous block's MFMAs
-    {
-      const bool one_chunk = s0 + kKB <= pc.split || s0 >= pc.split;
-      const bool simple = pc.mapped && s0 + kKB <= pc.valid && one_chunk;
-      const int cs = s0 >= pc.split ? 1 : 0;
-      if (simple) {
-        if (pc.vcheck) decode_block<kD, true, true>(pc, s0, cs, rc, Mu, Ks, Vt);
-        else decode_block<kD, false, true>(pc, s0, cs, rc, Mu, Ks, Vt);
-      } else {
-        if (pc.vcheck) decode_block<kD, true, false>(pc, s0, 0, rc, Mu, Ks, Vt);
-        else decode_block<kD, false, false>(pc, s0, 0, rc, Mu, Ks, Vt);
-      }
+    PageInfo pc = page_info(g, n_phys, pages, b0 / bpp, n_pages, last_tokens);
+    BlockRaw<Shape<kD>::kKPT> rn;
+    fetch_block<kD>(g, pc, h, (b0 % bpp) * kKB, rn);
+    if (tid < 2 * kD) Mb[(b0 & 1) * 2 * kD + tid] = rn.mu;
+    __syncthreads();
+    decode_any<kD>(pc, (b0 % bpp) * kKB, rn, Mb + (b0 & 1) * 2 * kD, Kb + (b0 & 1) * kKsElems,
+                   Vb + (b0 & 1) * kVtElems);
+    PageInfo pn = pc;
+    if (b0 + 1 < b1) {
+      if ((b0 + 1) % bpp == 0) pn = page_info(g, n_phys, pages, (b0 + 1) / bpp, n_pages, last_tokens);
+      fetch_block<kD>(g, pn, h, ((b0 + 1) % bpp) * kKB, rn);
+      if (tid < 2 * kD) Mb[((b0 + 1) & 1) * 2 * kD + tid] = rn.mu;
     }
     __syncthreads();
 
-    // S^T tiles: keys 32 kt + (r / 4) * 8 + 4 half + r % 4 of this block, query lane % 32
-    // (the two key tiles' MFMA chains alternate, sharing each Q fragment)
-    f32x16 st[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[kt][r] = 0.0f;
-    {
-      const uint16_t* kp = Ks + (lane & 31) * kKsRow + 8 * half;
-      const uint16_t* qs = Qs + (wave * 32 + (lane & 31)) * kKsRow + 8 * half;
-#pragma unroll
-      for (int s = 0; s < kD / 16; ++s) {
-        const bf16x8 qv = as_bf16x8(*(const u32x4*)(qs + 16 * s));
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-          st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              as_bf16x8(*(const u32x4*)(kp + 32 * kt * kKsRow + 16 * s)), qv, st[kt], 0, 0, 0);
-      }
-    }
-    // online softmax for this lane's query (keys split between lane and lane ^ 32),
-    // in log2 units: t = S c with c = |scale| log2(e) >= 0, so the block max of t is
-    // RN(c max S) and each weight is exp2(fma(S, c, -m)).  Keys past the last
-    // valid slot only occur in a block that is not full (uniform test).
-    const bool full = s0 + kKB <= pc.valid;
-    float mb = -__builtin_inff();
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kt + (r >> 2) * 8 + 4 * half + (r & 3);
-        if (full || s0 + key < pc.valid) mb = fmaxf(mb, st[kt][r]);
-      }
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    const float m_new = fmaxf(m, mb * scale_log2e);         // finite: the block has a valid key
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first block
-    float ps = 0.0f;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kt + (r >> 2) * 8 + 4 * half + (r & 3);
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kt][r], scale_log2e, -m_new));
-        if (!full && s0 + key >= pc.valid) p = 0.0f;
-        st[kt][r] = p;
-        ps += p;
-      }
-    ps += __shfl_xor(ps, 32, 64);
-    l = l * alpha + ps;
-    m = m_new;
-    if (__any(alpha != 1.0f)) {                             // the running max moved
-#pragma unroll
-      for (int dt = 0; dt < kD / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    }
-
-    // O^T += V^T P^T.  Step kk of key tile kt: k index j of lane half `half` is
-    // key 32 kt + 16 kk + (j / 4) * 8 + 4 half + j % 4 = S^T register 8 kk + j.
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        u32x4 pb;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pb[j] = pack_bf16x2(st[kt][8 * kk + 2 * j], st[kt][8 * kk + 2 * j + 1]);
-#pragma unroll
-        for (int dt = 0; dt < kD / 32; ++dt) {
-          const uint16_t* vp = Vt + (32 * dt + (lane & 31)) * kVtRow + 32 * kt + 16 * kk + 4 * half;
-          const u32x2 v0 = *(const u32x2*)vp, v1 = *(const u32x2*)(vp + 8);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              as_bf16x8(u32x4{v0[0], v0[1], v1[0], v1[1]}), as_bf16x8(pb), o[dt], 0, 0, 0);
+    for (int b = b0; b < b1; ++b) {
+      const int cur = b & 1, nxt = cur ^ 1;
+      const int s0 = (b % bpp) * kKB;
+      const bool has1 = b + 1 < b1, has2 = b + 2 < b1;
+      PageInfo pn2 = pn;
+      if (has2 && (b + 2) % bpp == 0)
+        pn2 = page_info(g, n_phys, pages, (b + 2) / bpp, n_pages, last_tokens);
+      const auto decode_next = [&]() {
+        if (has1) {
+          decode_any<kD>(pn, ((b + 1) % bpp) * kKB, rn, Mb + nxt * 2 * kD, Kb + nxt * kKsElems,
+                         Vb + nxt * kVtElems);
+          if (has2) fetch_block<kD>(g, pn2, h, ((b + 2) % bpp) * kKB, rn);
         }
-      }
+      };
+      if (pc.valid > s0)                                     // block holds a key (uniform)
+        attend_block<kD>(Kb + cur * kKsElems, Vb + cur * kVtElems, qr, lane, s0, pc.valid,
+                         scale_log2e, m, l, o, decode_next);
+      else
+        decode_next();
+      // K means of block b + 2 into the Mu buffer that block b's decode used
+      if (has2 && tid < 2 * kD) Mb[cur * 2 * kD + tid] = rn.mu;
+      __syncthreads();
+      pc = pn;
+      pn = pn2;
     }
   }
 
