@@ -411,7 +411,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int h = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5;
-  const int64_t qrow = (int64_t)blockIdx.x * kQB + wave * 32 + (lane & 31);
+  const int64_t wave_q0 = (int64_t)blockIdx.x * kQB + wave * 32;   // the wave's first query
+  const int64_t qrow = wave_q0 + (lane & 31);
 
   // The lane's query row in registers, as the B operand of S^T = K^ Q^T:
   // step s covers channels 16 s .. 16 s + 15, lane half `half` the 8 channels
@@ -473,7 +474,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           if (has2) fetch_block<kD>(g, pn2, h, ((b + 2) % bpp) * kKB, rn);
         }
       };
-      if (pc.valid > s0)                                     // block holds a key (uniform)
+      // a block with a key, for a wave with a query (both uniform per wave: the
+      // waves past the last query only help decode)
+      if (pc.valid > s0 && wave_q0 < n_q)
         attend_block<kD>(Kb + cur * kKsElems, Vb + cur * kVtElems, qr, lane, s0, pc.valid,
                          scale_log2e, m, l, o, decode_next);
       else
