@@ -97,9 +97,13 @@ struct PageInfo {
   int vcheck;             // a V^ product of this page may need the bf16 midpoint fix-up
 };
 
+// `prev`: the facts of the page before, when `has_prev` (consecutive pages
+// usually hold the same chunks, whose V scale test is then reused instead of
+// recomputed).
 __device__ __forceinline__ PageInfo page_info(const KvGeom& g, int64_t n_phys,
                                               const int32_t* pages, int pi, int n_pages,
-                                              int last_tokens) {
+                                              int last_tokens, const PageInfo& prev,
+                                              bool has_prev) {
   PageInfo p;
   const int32_t lp = pages[pi];
   bool mapped = lp >= 0 && lp < g.max_pages;
@@ -117,7 +121,10 @@ __device__ __forceinline__ PageInfo page_info(const KvGeom& g, int64_t n_phys,
   p.sgk1 = g.k_gscale[p.c1];
   p.sgv0 = g.v_gscale[p.c0];
   p.sgv1 = g.v_gscale[p.c1];
-  p.vcheck = product_needs_check(p.sgv0) || product_needs_check(p.sgv1);
+  if (has_prev && prev.sgv0 == p.sgv0 && prev.sgv1 == p.sgv1)
+    p.vcheck = prev.vcheck;
+  else
+    p.vcheck = product_needs_check(p.sgv0) || product_needs_check(p.sgv1);
   return p;
 }
 
@@ -445,7 +452,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // MFMAs and its softmax, decodes block b + 1 and then reuses rn to fetch
   // block b + 2; one barrier ends it.
   if (b0 < b1) {
-    PageInfo pc = page_info(g, n_phys, pages, b0 / bpp, n_pages, last_tokens);
+    PageInfo pc;
+    pc = page_info(g, n_phys, pages, b0 / bpp, n_pages, last_tokens, pc, false);
     BlockRaw<Shape<kD>::kKPT> rn;
     fetch_block<kD>(g, pc, h, (b0 % bpp) * kKB, rn);
     if (tid < 2 * kD) Mb[(b0 & 1) * 2 * kD + tid] = rn.mu;
@@ -454,7 +462,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                    Vb + (b0 & 1) * kVtElems);
     PageInfo pn = pc;
     if (b0 + 1 < b1) {
-      if ((b0 + 1) % bpp == 0) pn = page_info(g, n_phys, pages, (b0 + 1) / bpp, n_pages, last_tokens);
+      if ((b0 + 1) % bpp == 0)
+        pn = page_info(g, n_phys, pages, (b0 + 1) / bpp, n_pages, last_tokens, pc, true);
       fetch_block<kD>(g, pn, h, ((b0 + 1) % bpp) * kKB, rn);
       if (tid < 2 * kD) Mb[((b0 + 1) & 1) * 2 * kD + tid] = rn.mu;
     }
@@ -466,7 +475,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const bool has1 = b + 1 < b1, has2 = b + 2 < b1;
       PageInfo pn2 = pn;
       if (has2 && (b + 2) % bpp == 0)
-        pn2 = page_info(g, n_phys, pages, (b + 2) / bpp, n_pages, last_tokens);
+        pn2 = page_info(g, n_phys, pages, (b + 2) / bpp, n_pages, last_tokens, pn, true);
       const auto decode_next = [&]() {
         if (has1) {
           decode_any<kD>(pn, ((b + 1) % bpp) * kKB, rn, Mb + nxt * 2 * kD, Kb + nxt * kKsElems,
