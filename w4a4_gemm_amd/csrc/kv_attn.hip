@@ -17,8 +17,8 @@
 //   S^T = K^ Q^T    (32 keys x 32 queries per v_mfma_f32_32x32x16_bf16 tile)
 //   O^T += V^T P^T  (32 channels x 32 queries per tile)
 // so that in both accumulators a lane owns one query (column lane % 32) and
-// its registers run over keys or channels.  The online softmax (running max
-// m, running sum l, rescaling of O) is then per lane plus one exchange with
+// its registers run over keys or channels.  The online softmax (reference
+// max m, running sum l, rescaling of O) is then per lane plus one exchange with
 // lane ^ 32 (a permlane swap), and P goes from the S^T registers straight into the second
 // MFMA: the MFMA sums over its 16 k values in any order, so the k order of
 // a step is taken to be the key order of the S^T registers, and V^T is read
@@ -46,6 +46,7 @@ constexpr int kQB = 32 * kWaves;          // queries per workgroup
 constexpr int kKB = 64;               // keys per block
 constexpr int kVtRow = kKB + 8;       // bf16 per V^T row in LDS (144 bytes)
 constexpr int kMaxD = 128;            // largest head_dim (sizes the split workspace)
+constexpr float kLazy = 8.0f;         // slack of the softmax reference max (log2 units)
 
 // Head-dim dependent shapes (head_dim kD = 64 or 128).
 template <int kD>
@@ -297,7 +298,7 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ Kc,
   decode_next();
   // online softmax for this lane's query (keys split between lane and lane ^ 32),
   // in log2 units: t = S c with c = |scale| log2(e) >= 0, so the block max of t is
-  // RN(c max S) and each weight is exp2(fma(S, c, -m)).  Keys past the last
+  // RN(c max S) and each weight is exp2(fma(S, c, -m)) for the reference m.  Keys past the last
   // valid slot only occur in a block that is not full: a full block (the
   // usual case, a uniform test) takes a loop without per-key masks.  (This
   // file is compiled without NaN support, so fmaxf is one instruction.)
@@ -318,7 +319,11 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ Kc,
       }
   }
   mb = max_lane32(mb);
-  const float m_new = fmaxf(m, mb * scale_log2e);          // finite: the block has a valid key
+  // m is a reference, not always the running max: it moves only when a block's
+  // max exceeds it by more than kLazy (log2 units), so weights stay below
+  // 2^kLazy (exact in scale for bf16 and fp32) and O is rescaled rarely.
+  const float bmax = mb * scale_log2e;                    // finite: the block has a valid key
+  const float m_new = bmax > m + kLazy ? bmax : m;         // the first block always moves m
   const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first block
   float ps = 0.0f;
   if (full) {
@@ -345,7 +350,7 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ Kc,
   ps = sum_lane32(ps);
   l = l * alpha + ps;
   m = m_new;
-  if (__any(alpha != 1.0f)) {                             // the running max moved
+  if (__any(alpha != 1.0f)) {                             // a reference moved
 #pragma unroll
     for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
@@ -393,7 +398,7 @@ __device__ __forceinline__ void decode_any(const PageInfo& p, int s0,
 
 // Split `split` of `n_split` handles key blocks [b0, b1) of the window.  With
 // one split the result is normalized and written as bf16; otherwise the
-// unnormalized fp32 O^T, the running max m (log2 units) and the sum l go to
+// unnormalized fp32 O^T, the reference max m (log2 units) and the sum l go to
 // the workspace: O at part + ((split * n_q + n) * H + h) * D, (m, l) after all
 // O values.
 // Two waves per SIMD (registers capped at 256 per lane): one wave's softmax
