@@ -474,8 +474,17 @@ __global__ __launch_bounds__(512) void kv_dequant_kernel(KvGeom g, int64_t n_phy
   const int upr = D / 8;                                  // units per (token, head) row
   const int npos = H * upr;                               // units per token
   const int tiles = (P + kTT - 1) / kTT;
-  const int64_t i = blockIdx.x / tiles;
-  const int t0 = (blockIdx.x % tiles) * kTT;
+  // Workgroup b runs on XCD b % 8.  Tiles 2j and 2j + 1 share the 128-byte
+  // lines of their heads' scale bytes (16 tokens x 8 bytes), so they are given
+  // to workgroups b and b + 8 -- the same XCD, dispatched back to back -- and
+  // the line is fetched into that XCD's L2 once instead of into two.
+  int bid = blockIdx.x;
+  if ((gridDim.x & 15u) == 0) {
+    const int x = bid & 7, s = bid >> 3;
+    bid = (s >> 1) * 16 + x * 2 + (s & 1);
+  }
+  const int64_t i = bid / tiles;
+  const int t0 = (bid % tiles) * kTT;
   const int ntok = min(kTT, P - t0);
   const int32_t lp = pages[i];
   bool valid = lp >= 0 && lp < g.max_pages;
