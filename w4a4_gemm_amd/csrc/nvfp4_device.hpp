@@ -353,7 +353,12 @@ __device__ __forceinline__ void kv_unit_bf16(uint32_t kcw, uint32_t ksb, uint32_
   }
   if (__builtin_expect(off == 0u, 0)) {
 #pragma unroll
-    for (int n = 0; n < 8; ++n) kf[n] = fma_for_bf16(ka[n], sgk, mu[n]);
+    for (int n = 0; n < 8; ++n) {
+      // (the barrier keeps this rare path's fp64 conversion of mu inside it)
+      float mun = mu[n];
+      __asm__ volatile("" : "+v"(mun));
+      kf[n] = fma_for_bf16(ka[n], sgk, mun);
+    }
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
