@@ -533,27 +533,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 // Merge the splits of one (query, head) row: M = max m_s, L = sum l_s 2^(m_s - M),
 // O = sum O_s 2^(m_s - M) / L, rounded once to bf16.  One wave per row, kD / 64
-// channels per lane.
+// channels per lane.  Splits are read kChunk at a time with all their loads in
+// flight; the sums still run over s in increasing order.
 template <int kD>
 __global__ __launch_bounds__(256) void kv_attention_combine(const float* __restrict__ part,
                                                             int n_split, int64_t rows,
                                                             uint16_t* __restrict__ out) {
   constexpr int kCpl = kD / 64;                             // channels per lane: 1 or 2
+  constexpr int kChunk = 8;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
   const float* ml = part + (int64_t)n_split * rows * kD;
   float M = -__builtin_inff();
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, ml[((int64_t)s * rows + row) * 2]);
+  for (int s0 = 0; s0 < n_split; s0 += kChunk) {
+    float mv[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i)
+      mv[i] = s0 + i < n_split ? ml[((int64_t)(s0 + i) * rows + row) * 2] : -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) M = fmaxf(M, mv[i]);
+  }
   float L = 0.0f, a[kCpl] = {};
   if (M != -__builtin_inff()) {
-    for (int s = 0; s < n_split; ++s) {
-      const f32x2 v = *(const f32x2*)(ml + ((int64_t)s * rows + row) * 2);
-      const float w = __builtin_amdgcn_exp2f(v[0] - M);    // 0 for an empty split (m = -inf)
-      const float* os = part + ((int64_t)s * rows + row) * kD + kCpl * lane;
-      L += v[1] * w;
+    for (int s0 = 0; s0 < n_split; s0 += kChunk) {
+      f32x2 v[kChunk];
+      float ov[kChunk][kCpl];
 #pragma unroll
-      for (int c = 0; c < kCpl; ++c) a[c] += os[c] * w;
+      for (int i = 0; i < kChunk; ++i) {
+        const int64_t s = s0 + i;
+        if (s < n_split) {
+          v[i] = *(const f32x2*)(ml + (s * rows + row) * 2);
+          const float* os = part + (s * rows + row) * kD + kCpl * lane;
+#pragma unroll
+          for (int c = 0; c < kCpl; ++c) ov[i][c] = os[c];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        if (s0 + i < n_split) {
+          const float w = __builtin_amdgcn_exp2f(v[i][0] - M);   // 0 for an empty split (m = -inf)
+          L += v[i][1] * w;
+#pragma unroll
+          for (int c = 0; c < kCpl; ++c) a[c] += ov[i][c] * w;
+        }
+      }
     }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
