@@ -91,6 +91,38 @@ def test_constant_chunk_and_layers():
     assert float(gpu.k_gscale[1, 0].cpu()) == 1.0
 
 
+def test_k_mean_exact_over_wide_ranges():
+    """K means of channels whose values span more binades than an fp64 sum keeps:
+    the stats pass flags them and the finalize sums them exactly as integers
+    (design reading 18).  Head 0 channel 0 mixes +-2^50 and 2^-50, 2^-60 values;
+    channel 1 alternates +-2^100 (they cancel) with tiny values between, so its
+    mean comes from the tiny ones alone; head 1 channel 5 mixes +-1 with a bf16
+    subnormal, so its mean is an fp32 subnormal."""
+    h, d, p, t = 2, 64, 64, 300
+    table = np.arange(5, dtype=np.int32)[None, :]
+    gpu, ora = _pair(1, h, d, p, 5, 1, table, 5)
+    kb, vb = synth.kv_chunk(t=t, h=h, d=d, seed_k=11, seed_v=12, seed_off=13)
+    k = synth.bf16_bits_to_f32(kb).astype(np.float64).reshape(t, h, d)
+    rng = np.random.default_rng(14)
+    k[:, 0, 0] = rng.choice([1.5 * 2.0 ** 50, -1.25 * 2.0 ** 50, 1.125 * 2.0 ** -50,
+                             -1.75 * 2.0 ** -60], size=t)
+    k[:, 0, 1] = np.where(np.arange(t) % 2 == 0, 2.0 ** 100, -(2.0 ** 100))
+    k[10:20, 0, 1] = np.array([1, 3, 5, 7, 9, 11, 13, 15, 17, 19]) * 2.0 ** -100
+    k[:, 1, 5] = np.where(np.arange(t) % 2 == 0, 1.0, -1.0)
+    k[100:104, 1, 5] = 2.0 ** -130                        # bf16 subnormals
+    kb2 = synth.to_bf16_bits(k.astype(np.float32)).reshape(kb.shape)
+    assert np.array_equal(synth.bf16_bits_to_f32(kb2).astype(np.float64).reshape(t, h, d), k)
+    # an fp64 running sum in token order loses the small terms of channel 1
+    import math
+    assert sum(k[:, 0, 1]) != math.fsum(k[:, 0, 1])
+    _write(gpu, ora, 0, 0, kb2, vb, 0)
+    _compare_state(gpu, ora, 0, [0], list(range(5)))
+    _compare_dequant(gpu, ora, 0, [0, 3, 4])
+    mu = gpu.k_mean[0, 0].cpu().numpy().reshape(h, d)
+    assert mu[0, 1] != 0.0 and abs(mu[0, 1]) < 2.0 ** -90
+    assert 0.0 < mu[1, 5] < 2.0 ** -126                    # an fp32 subnormal
+
+
 def test_invalid_listed_pages_give_zeros():
     h, d, p = 2, 64, 32
     gpu, ora = _pair(1, h, d, p, 4, 1, np.array([[0, 1, 2, 3]], np.int32), 4)

@@ -3,9 +3,12 @@
 // Write path (techwalker.com LongLive-2.0 report summary, section 四, second
 // key: K is mean-subtracted, then K and V are stored in NVFP4; zuobiaodaohang
 // LongLive blog: the quantized cache is updated in place):
-//   1. kv_stats:     one read of K and V: per (head, channel) fp64 sum, min and
-//                    max of K over a token slice; per workgroup max|V|.
-//   2. kv_finalize:  per channel mu = RN32(S / T); max|K - mu| from min/max
+//   1. kv_stats:     one read of K and V: per (head, channel) fp64 sum, min,
+//                    max and smallest nonzero |K| over a token slice; per
+//                    workgroup max|V|.
+//   2. kv_finalize:  per channel mu = RN32(S / T) (S exact: the fp64 sum when
+//                    the channel's range allows, else an integer sum of the
+//                    channel); max|K - mu| from min/max
 //                    (RN32 is monotone, so max |RN32(K - mu)| is
 //                    max(RN32(Kmax - mu), RN32(mu - Kmin))); mu is stored.
 //   3. kv_quantize:  second read (usually from the 256 MB Infinity Cache):
@@ -27,11 +30,13 @@ namespace {
 constexpr int kStatsSlices = 32;          // token slices of the stats pass
 constexpr int kStatsCols = 64;            // channels per stats workgroup (8 lanes x 8)
 constexpr int kFinalizeThreads = 256;
+static_assert(kStatsSlices % 8 == 0, "the finalize folds the slices eight at a time");
 
 struct KvWorkspace {
   double* sum;      // [slices][C]
   float* kmin;      // [slices][C]
   float* kmax;      // [slices][C]
+  uint32_t* knz;    // [slices][C]: smallest nonzero |K| as fp32 bits, minus one (all ones: none)
   float* vamax;     // [stats workgroups]
   float* kamax;     // [finalize workgroups]
   float* vamax_f;   // [finalize workgroups]: the stats partials of V folded per finalize workgroup
@@ -48,6 +53,8 @@ KvWorkspace carve(void* ws, int64_t C, int n_stats_wg, int n_fin_wg) {
   p += round256(sizeof(float) * kStatsSlices * C);
   w.kmax = (float*)p;
   p += round256(sizeof(float) * kStatsSlices * C);
+  w.knz = (uint32_t*)p;
+  p += round256(sizeof(uint32_t) * kStatsSlices * C);
   w.vamax = (float*)p;
   p += round256(sizeof(float) * n_stats_wg);
   w.kamax = (float*)p;
@@ -64,7 +71,7 @@ int finalize_wgs(int64_t C) { return (int)((C + kFinalizeThreads - 1) / kFinaliz
 size_t kv_quantize_workspace_bytes(int64_t T, int64_t H, int64_t D) {
   (void)T;
   const int64_t C = H * D;
-  return round256(sizeof(double) * kStatsSlices * C) + 2 * round256(sizeof(float) * kStatsSlices * C) +
+  return round256(sizeof(double) * kStatsSlices * C) + 3 * round256(sizeof(float) * kStatsSlices * C) +
          round256(sizeof(float) * stats_wgs(C)) + 2 * round256(sizeof(float) * finalize_wgs(C));
 }
 
@@ -84,9 +91,15 @@ __global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t* __restric
   const int64_t t0 = slice * per, t1 = t0 + per < T ? t0 + per : T;
   double s[8];
   float mn[8], mx[8];
+  uint32_t nz[8];        // smallest nonzero |K| bits minus one (zero wraps to all ones)
   uint32_t va = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) { s[j] = 0.0; mn[j] = __builtin_inff(); mx[j] = -__builtin_inff(); }
+  for (int j = 0; j < 8; ++j) {
+    s[j] = 0.0;
+    mn[j] = __builtin_inff();
+    mx[j] = -__builtin_inff();
+    nz[j] = 0xFFFFFFFFu;
+  }
   const bool active = c0 < C;
   if (active && t0 < t1) {
     // kStatsUnroll tokens' loads in flight per lane; a token past the slice
@@ -112,6 +125,8 @@ __global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t* __restric
           mn[2 * j + 1] = fminf(mn[2 * j + 1], b);
           mx[2 * j] = fmaxf(mx[2 * j], a);
           mx[2 * j + 1] = fmaxf(mx[2 * j + 1], b);
+          nz[2 * j] = min(nz[2 * j], (__float_as_uint(a) & 0x7FFFFFFFu) - 1u);
+          nz[2 * j + 1] = min(nz[2 * j + 1], (__float_as_uint(b) & 0x7FFFFFFFu) - 1u);
           const uint32_t av = vw[u][j] & 0x7FFF7FFFu;
           va = max(va, max(av & 0xFFFFu, av >> 16));
         }
@@ -148,6 +163,20 @@ __global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t* __restric
       ws.kmax[slice * C + c] = hi;
     }
   }
+  // the smallest nonzero |K| through smin's space once it has been read (an
+  // array of its own would cost a resident workgroup per CU)
+  __syncthreads();
+  uint32_t(*snz)[kStatsCols + 1] = (uint32_t(*)[kStatsCols + 1])smin;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) snz[tl][cl * 8 + j] = nz[j];
+  __syncthreads();
+  if (threadIdx.x < kStatsCols) {
+    const int ch = threadIdx.x;
+    uint32_t z = 0xFFFFFFFFu;
+    for (int i = 0; i < 32; ++i) z = min(z, snz[i][ch]);
+    const int64_t c = (int64_t)cg * kStatsCols + ch;
+    if (c < C) ws.knz[slice * C + c] = z;
+  }
   if (threadIdx.x == 0)
     ws.vamax[blockIdx.x] = fmaxf(fmaxf(svmax[0], svmax[1]), fmaxf(svmax[2], svmax[3]));
 }
@@ -174,22 +203,151 @@ __device__ __forceinline__ float mean_rn32(double S, int64_t T) {
   return f;
 }
 
+// The exact sum for a channel whose values span too many binades for fp64:
+// every bf16 value is m 2^(max(E, 1) - 134) with m < 2^8 (E the exponent
+// field), so S is an integer in units of 2^-133 below 2^(8 + 254 + log2 T);
+// positive and negative parts are summed in five 64-bit limbs each.
+__device__ __forceinline__ void add_shifted(uint64_t (&a)[5], uint32_t m, int sh) {
+  const int limb = sh >> 6, off = sh & 63;
+  const uint64_t lo = (uint64_t)m << off;
+  const uint64_t hi = off > 56 ? (uint64_t)m >> (64 - off) : 0;
+  uint64_t carry = 0;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const uint64_t add = i == limb ? lo : (i == limb + 1 ? hi : 0);
+    const uint64_t s1 = a[i] + add;
+    const uint64_t s2 = s1 + carry;
+    carry = (uint64_t)(s1 < add) | (uint64_t)(s2 < carry);
+    a[i] = s2;
+  }
+}
+
+// mu = RN32(S / T) for channel c of K ([T][C] bf16) from the exact integer sum:
+// the top 64 bits N of |S| (the rest folded into a sticky bit) are divided by
+// T, which leaves at least 25 quotient bits for T < 2^39, and the quotient is
+// rounded to fp32 (ties to even, subnormal results included).  One thread per
+// channel reads the channel's T values; it runs only for channels that fail
+// the fp64 exactness test below.
+// limb j of a (a select over the five, so the limbs stay in registers)
+__device__ __forceinline__ uint64_t pick(const uint64_t (&a)[5], int j) {
+  uint64_t v = 0;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) v = i == j ? a[i] : v;
+  return v;
+}
+
+__device__ __forceinline__ float exact_mean(const uint16_t* __restrict__ k, int64_t T, int64_t C,
+                                            int64_t c) {
+  uint64_t P[5] = {0, 0, 0, 0, 0}, N[5] = {0, 0, 0, 0, 0};
+  for (int64_t t = 0; t < T; ++t) {
+    const uint32_t u = k[t * C + c];
+    const uint32_t mag = u & 0x7FFFu, E = mag >> 7;
+    if (mag == 0) continue;
+    const uint32_t m = (mag & 0x7Fu) | (E ? 0x80u : 0u);
+    const int sh = (int)(E ? E : 1u) - 1;
+    if (u & 0x8000u) add_shifted(N, m, sh);
+    else add_shifted(P, m, sh);
+  }
+  bool neg = false;
+  for (int i = 4; i >= 0; --i) {
+    if (P[i] != N[i]) {
+      neg = N[i] > P[i];
+      break;
+    }
+  }
+  uint64_t D[5];
+  uint64_t borrow = 0;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const uint64_t x = neg ? N[i] : P[i], y = neg ? P[i] : N[i];
+    const uint64_t d1 = x - y, d2 = d1 - borrow;
+    borrow = (uint64_t)(x < y) | (uint64_t)(d1 < borrow);
+    D[i] = d2;
+  }
+  int top = -1;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) top = D[i] != 0 ? i : top;
+  if (top < 0) return 0.0f;
+  const int n = 64 * top + (64 - __builtin_clzll(pick(D, top)));   // bit length of |S|
+  uint64_t Nt;
+  bool sticky = false;
+  if (n <= 64) {
+    Nt = D[0] << (64 - n);
+  } else {
+    const int sft = n - 64, li = sft >> 6, lo = sft & 63;
+    const uint64_t dl = pick(D, li), dh = pick(D, li + 1);
+    Nt = lo ? (dl >> lo) | (dh << (64 - lo)) : dl;
+    sticky = lo ? (dl & ((1ull << lo) - 1)) != 0 : false;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) sticky = sticky || (i < li && D[i] != 0);
+  }
+  const uint64_t Tu = (uint64_t)T, Q = Nt / Tu, R = Nt % Tu;
+  const bool st = sticky || R != 0;
+  const int qb = 64 - __builtin_clzll(Q);
+  const int lsb = n - 197;                                          // exponent of Q's last bit
+  const int target = max(qb - 1 + lsb - 23, -149);                  // exponent of the fp32 ulp
+  const int shift = target - lsb;                                   // >= 1
+  uint32_t mant;
+  if (shift >= 65) {
+    mant = 0;
+  } else if (shift == 64) {
+    mant = (Q > (1ull << 63) || (Q == (1ull << 63) && st)) ? 1u : 0u;
+  } else {
+    mant = (uint32_t)(Q >> shift);
+    const uint64_t rem = Q & ((1ull << shift) - 1), half = 1ull << (shift - 1);
+    if (rem > half || (rem == half && (st || (mant & 1u)))) ++mant;
+  }
+  const float f = ldexpf((float)mant, target);
+  return neg ? -f : f;
+}
+
 // Each workgroup also folds its share of the stats pass's V maxima, so the
 // quantize pass reads 2 x (finalize workgroups) partials for both tensor scales.
-__global__ __launch_bounds__(kFinalizeThreads) void kv_finalize_kernel(KvWorkspace ws, int64_t T,
-                                                                      int64_t C, int n_stats_wg,
+// The fp64 sums are exact when every partial sum fits 53 bits above the last
+// bit of the channel's smallest nonzero value: every value is a multiple of
+// u = 2^(max(Emin, 1) - 134) and every partial sum is below T 2^(Emax - 126),
+// so Emax - max(Emin, 1) + ceil(log2 T) <= 45 suffices.  Other channels take
+// exact_mean.
+__global__ __launch_bounds__(kFinalizeThreads) void kv_finalize_kernel(KvWorkspace ws,
+                                                                      const uint16_t* __restrict__ k,
+                                                                      int64_t T, int64_t C,
+                                                                      int n_stats_wg,
                                                                       float* __restrict__ mu_out) {
   const int64_t c = (int64_t)blockIdx.x * kFinalizeThreads + threadIdx.x;
   float amax = 0.0f;
   if (c < C) {
     double S = 0.0;
     float lo = __builtin_inff(), hi = -__builtin_inff();
-    for (int i = 0; i < kStatsSlices; ++i) {
-      S += ws.sum[i * C + c];
-      lo = fminf(lo, ws.kmin[i * C + c]);
-      hi = fmaxf(hi, ws.kmax[i * C + c]);
+    uint32_t z = 0xFFFFFFFFu;
+    // eight slices' partials loaded before any is folded (all loads in flight)
+    for (int i0 = 0; i0 < kStatsSlices; i0 += 8) {
+      double sv[8];
+      float lv[8], hv[8];
+      uint32_t zv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t o = (int64_t)(i0 + u) * C + c;
+        sv[u] = ws.sum[o];
+        lv[u] = ws.kmin[o];
+        hv[u] = ws.kmax[o];
+        zv[u] = ws.knz[o];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        S += sv[u];
+        lo = fminf(lo, lv[u]);
+        hi = fmaxf(hi, hv[u]);
+        z = min(z, zv[u]);
+      }
     }
-    const float mu = mean_rn32(S, T);
+    bool exact = true;
+    if (z != 0xFFFFFFFFu) {
+      const int emax = (int)(__float_as_uint(fmaxf(fabsf(lo), fabsf(hi))) >> 23);
+      const int emin = (int)((z + 1u) >> 23);
+      const int lg_t = T > 1 ? 64 - __builtin_clzll((uint64_t)(T - 1)) : 0;
+      exact = emax - (emin > 1 ? emin : 1) + lg_t <= 45;
+    }
+    const float mu = exact ? mean_rn32(S, T) : exact_mean(k, T, C, c);
     mu_out[c] = mu;
     amax = fmaxf(hi - mu, mu - lo);              // each an RN32 of an exact difference
   }
@@ -719,8 +877,8 @@ void launch_kv_quantize(const KvGeom& g, int32_t chunk_id, const uint16_t* k, co
   KvWorkspace ws = carve(workspace, C, nsw, nfw);
   float* mu = g.k_mean + (int64_t)chunk_id * C;
   hipLaunchKernelGGL(kv_stats_kernel, dim3(nsw), dim3(256), 0, stream, k, v, T, C, ws);
-  hipLaunchKernelGGL(kv_finalize_kernel, dim3(nfw), dim3(kFinalizeThreads), 0, stream, ws, T, C,
-                     nsw, mu);
+  hipLaunchKernelGGL(kv_finalize_kernel, dim3(nfw), dim3(kFinalizeThreads), 0, stream, ws, k, T,
+                     C, nsw, mu);
   const int D = g.head_dim;
   const bool small = T * g.n_heads * D < (int64_t(1) << 31) &&
                      start_token + T < (int64_t(1) << 31) &&
