@@ -222,12 +222,6 @@ __device__ __forceinline__ void add_shifted(uint64_t (&a)[5], uint32_t m, int sh
   }
 }
 
-// mu = RN32(S / T) for channel c of K ([T][C] bf16) from the exact integer sum:
-// the top 64 bits N of |S| (the rest folded into a sticky bit) are divided by
-// T, which leaves at least 25 quotient bits for T < 2^39, and the quotient is
-// rounded to fp32 (ties to even, subnormal results included).  One thread per
-// channel reads the channel's T values; it runs only for channels that fail
-// the fp64 exactness test below.
 // limb j of a (a select over the five, so the limbs stay in registers)
 __device__ __forceinline__ uint64_t pick(const uint64_t (&a)[5], int j) {
   uint64_t v = 0;
@@ -236,17 +230,55 @@ __device__ __forceinline__ uint64_t pick(const uint64_t (&a)[5], int j) {
   return v;
 }
 
-__device__ __forceinline__ float exact_mean(const uint16_t* __restrict__ k, int64_t T, int64_t C,
-                                            int64_t c) {
+// a += the a of lane ^ off (exact: five-limb addition with carries)
+__device__ __forceinline__ void add_lane_xor(uint64_t (&a)[5], int off) {
+  uint64_t carry = 0;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)a[i], off, 64);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(a[i] >> 32), off, 64);
+    const uint64_t b = ((uint64_t)hi << 32) | lo;
+    const uint64_t s1 = a[i] + b;
+    const uint64_t s2 = s1 + carry;
+    carry = (uint64_t)(s1 < b) | (uint64_t)(s2 < carry);
+    a[i] = s2;
+  }
+}
+
+// mu = RN32(S / T) for channel c of K ([T][C] bf16) from the exact integer sum,
+// computed by the whole wave (every lane calls it with the same c; the result
+// is uniform): lane l sums tokens l, l + 64, ..., and the 64 partial sums are
+// added exactly across lanes.  The top 64 bits N of |S| (the rest folded into
+// a sticky bit) are divided by T, which leaves at least 25 quotient bits for
+// T < 2^39, and the quotient is rounded to fp32 (ties to even, subnormal
+// results included).  It runs only for channels that fail the fp64 exactness
+// test below.
+__device__ __forceinline__ float exact_mean_wave(const uint16_t* __restrict__ k, int64_t T,
+                                                 int64_t C, int64_t c, int lane) {
   uint64_t P[5] = {0, 0, 0, 0, 0}, N[5] = {0, 0, 0, 0, 0};
-  for (int64_t t = 0; t < T; ++t) {
-    const uint32_t u = k[t * C + c];
-    const uint32_t mag = u & 0x7FFFu, E = mag >> 7;
-    if (mag == 0) continue;
-    const uint32_t m = (mag & 0x7Fu) | (E ? 0x80u : 0u);
-    const int sh = (int)(E ? E : 1u) - 1;
-    if (u & 0x8000u) add_shifted(N, m, sh);
-    else add_shifted(P, m, sh);
+  constexpr int kU = 4;                                   // loads in flight per lane
+  for (int64_t t0 = lane; t0 < T; t0 += 64 * kU) {
+    uint32_t uv[kU];
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int64_t t = t0 + 64 * j;
+      uv[j] = t < T ? (uint32_t)k[t * C + c] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const uint32_t u = uv[j];
+      const uint32_t mag = u & 0x7FFFu, E = mag >> 7;
+      if (mag == 0) continue;
+      const uint32_t m = (mag & 0x7Fu) | (E ? 0x80u : 0u);
+      const int sh = (int)(E ? E : 1u) - 1;
+      if (u & 0x8000u) add_shifted(N, m, sh);
+      else add_shifted(P, m, sh);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    add_lane_xor(P, off);
+    add_lane_xor(N, off);
   }
   bool neg = false;
   for (int i = 4; i >= 0; --i) {
@@ -301,24 +333,25 @@ __device__ __forceinline__ float exact_mean(const uint16_t* __restrict__ k, int6
   return neg ? -f : f;
 }
 
-// Each workgroup also folds its share of the stats pass's V maxima, so the
-// quantize pass reads 2 x (finalize workgroups) partials for both tensor scales.
 // The fp64 sums are exact when every partial sum fits 53 bits above the last
 // bit of the channel's smallest nonzero value: every value is a multiple of
 // u = 2^(max(Emin, 1) - 134) and every partial sum is below T 2^(Emax - 126),
 // so Emax - max(Emin, 1) + ceil(log2 T) <= 45 suffices.  Other channels take
-// exact_mean.
+// exact_mean_wave.  Each workgroup also folds its share of the stats pass's V
+// maxima, so the quantize pass reads 2 x (finalize workgroups) partials for
+// both tensor scales.
 __global__ __launch_bounds__(kFinalizeThreads) void kv_finalize_kernel(KvWorkspace ws,
                                                                       const uint16_t* __restrict__ k,
                                                                       int64_t T, int64_t C,
                                                                       int n_stats_wg,
                                                                       float* __restrict__ mu_out) {
   const int64_t c = (int64_t)blockIdx.x * kFinalizeThreads + threadIdx.x;
+  const bool in = c < C;
   float amax = 0.0f;
-  if (c < C) {
-    double S = 0.0;
-    float lo = __builtin_inff(), hi = -__builtin_inff();
-    uint32_t z = 0xFFFFFFFFu;
+  double S = 0.0;
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+  uint32_t z = 0xFFFFFFFFu;
+  if (in) {
     // eight slices' partials loaded before any is folded (all loads in flight)
     for (int i0 = 0; i0 < kStatsSlices; i0 += 8) {
       double sv[8];
@@ -340,14 +373,26 @@ __global__ __launch_bounds__(kFinalizeThreads) void kv_finalize_kernel(KvWorkspa
         z = min(z, zv[u]);
       }
     }
-    bool exact = true;
-    if (z != 0xFFFFFFFFu) {
-      const int emax = (int)(__float_as_uint(fmaxf(fabsf(lo), fabsf(hi))) >> 23);
-      const int emin = (int)((z + 1u) >> 23);
-      const int lg_t = T > 1 ? 64 - __builtin_clzll((uint64_t)(T - 1)) : 0;
-      exact = emax - (emin > 1 ? emin : 1) + lg_t <= 45;
-    }
-    const float mu = exact ? mean_rn32(S, T) : exact_mean(k, T, C, c);
+  }
+  bool exact = true;
+  if (in && z != 0xFFFFFFFFu) {
+    const int emax = (int)(__float_as_uint(fmaxf(fabsf(lo), fabsf(hi))) >> 23);
+    const int emin = (int)((z + 1u) >> 23);
+    const int lg_t = T > 1 ? 64 - __builtin_clzll((uint64_t)(T - 1)) : 0;
+    exact = emax - (emin > 1 ? emin : 1) + lg_t <= 45;
+  }
+  float mu = in && exact ? mean_rn32(S, T) : 0.0f;
+  // channels whose fp64 sum may round: the wave sums each one exactly in turn
+  const int lane = threadIdx.x & 63;
+  uint64_t todo = __ballot(in && !exact);
+  while (todo) {
+    const int src = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    const int64_t cc = (int64_t)blockIdx.x * kFinalizeThreads + (threadIdx.x & ~63) + src;
+    const float m = exact_mean_wave(k, T, C, cc, lane);
+    if (lane == src) mu = m;
+  }
+  if (in) {
     mu_out[c] = mu;
     amax = fmaxf(hi - mu, mu - lo);              // each an RN32 of an exact difference
   }
