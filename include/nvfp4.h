@@ -253,9 +253,10 @@ int64_t nvfp4_kv_page_bytes(int32_t n_heads, int32_t head_dim, int32_t page_toke
  * c ended (so a page holds at most two chunks); chunk 0 starts on a page
  * boundary.  A chunk c > 0 that starts inside a page records that page's
  * earlier slots as chunk c - 1's.  The page table entries for
- * the touched pages must be valid physical pages.  The mean is accumulated in
- * fp64 in a fixed order; it is exact while the partial sums of a channel stay
- * within fp64's 53 bits (true for bf16 data of moderate dynamic range).
+ * the touched pages must be valid physical pages.  The mean is exact for every
+ * finite bf16 input: a channel is summed in fp64 when its values' range keeps
+ * every partial sum within fp64's 53 bits, else as an exact integer (a channel
+ * that needs it costs the call some 50 us).
  * Errors: EINVAL, ESHAPE (T < page_tokens unless it is chunk 0, chunk 0 not
  * starting on a page boundary, T >= 2^30, head_dim, token range past
  * max_pages, chunk_id >= max_chunks), EWORKSPACE. */

@@ -123,6 +123,32 @@ def test_k_mean_exact_over_wide_ranges():
     assert 0.0 < mu[1, 5] < 2.0 ** -126                    # an fp32 subnormal
 
 
+def test_k_mean_exact_full_chunk_with_tiny_values():
+    """The step's 7040-token chunk with three lone tiny K values (2^-40, -2^-35 and a bf16
+    subnormal) among values near 1-10: those channels fail the fp64 exactness test, so
+    their means come from the wave-wide integer sum; every mean, scale and page byte must
+    still match the oracle bit for bit."""
+    h, d, p = synth.KV_HEADS, synth.KV_HEAD_DIM, synth.KV_PAGE
+    table = synth.page_permutation(28, 33)[None, :]
+    gpu, ora = _pair(1, h, d, p, 28, 1, table, 28)
+    kb, vb = synth.kv_chunk()
+    k = synth.bf16_bits_to_f32(kb)
+    k[123, 5, 17] = 2.0 ** -40
+    k[4000, 20, 100] = -(2.0 ** -35)
+    k[77, 0, 0] = 2.0 ** -130
+    kb2 = synth.to_bf16_bits(k)
+    # the channels the finalize must take the exact path for (its test, on the host)
+    t = kb2.shape[0]
+    mag = (kb2.reshape(t, -1).astype(np.uint32) << 16) & 0x7FFFFFFF
+    emax = (mag.max(axis=0) >> 23).astype(np.int64)
+    emin = (np.where(mag == 0, 0xFFFFFFFF, mag).min(axis=0) >> 23).astype(np.int64)
+    flagged = np.nonzero(emax - np.maximum(emin, 1) + int(np.ceil(np.log2(t))) > 45)[0]
+    assert {5 * d + 17, 20 * d + 100, 0} <= set(flagged.tolist())
+    _write(gpu, ora, 0, 0, kb2, vb, 0)
+    _compare_state(gpu, ora, 0, [0], list(range(28)))
+    _compare_dequant(gpu, ora, 0, [0, 5, 27])
+
+
 def test_invalid_listed_pages_give_zeros():
     h, d, p = 2, 64, 32
     gpu, ora = _pair(1, h, d, p, 4, 1, np.array([[0, 1, 2, 3]], np.int32), 4)
