@@ -56,10 +56,8 @@ struct Shape {
   static constexpr int kKsRow = kD + 8;                  // bf16 per K^ row in LDS (conflict-free)
   static constexpr size_t kKsElems = (size_t)kKB * kKsRow;   // bf16 per K^ buffer
   static constexpr size_t kVtElems = (size_t)kD * kVtRow;    // bf16 per V^T buffer
-  static constexpr size_t kLds =                         // 2 x (K^ rows + V^T rows + K means)
-      2 * (2 * (kKsElems + kVtElems) + 2 * kD * 4);
+  static constexpr size_t kLds = 2 * 2 * (kKsElems + kVtElems);   // bytes: 2 x (K^ rows + V^T rows)
   static_assert(kKPT == 1 || kKPT == 2 || kKPT == 4, "a thread decodes 1, 2 or 4 keys of a block");
-  static_assert(kThreads >= 2 * kD, "one thread per K mean of the page's two chunks");
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -85,6 +83,38 @@ __device__ __forceinline__ int vt_pos(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
+// Offset (bf16) of position pos of V^T row `row` in a V^T buffer: the
+// row's 16-byte chunks are permuted, chunk pos / 8 stored at chunk
+// (pos / 8) ^ ((row / 16) % 8).  A decode write instruction covers rows
+// 8 u + c of the 16 channel groups u and, with unit_key0's key order, all
+// four dwords of one chunk: the permutation puts its 64 dwords in 64
+// distinct LDS banks (rows 8 apart alone would share 8).  The O^T reads
+// (16 lanes = 16 consecutive rows, one chunk) stay conflict-free: the 16
+// rows share one permutation.
+__device__ __forceinline__ int vt_index(int row, int pos) {
+  return row * kVtRow + 8 * ((pos >> 3) ^ ((row >> 4) & 7)) + (pos & 7);
+}
+
+// First key of this thread's decode units (kKPT adjacent keys; kGroups =
+// kD / 8 threads share a key run).  With two keys per thread the index of
+// the pair has bits 1 and 2 swapped, so that the four pairs of a wave are
+// keys {0, 2, 8, 10} + 4 (bit 0 of the wave) + 16 m: vt_pos makes them one
+// 16-byte chunk of each V^T row.
+template <int kKPT, int kGroups>
+__device__ __forceinline__ int unit_key0() {
+  int j = (int)threadIdx.x / kGroups;
+  if (kKPT == 2) j = (j & ~6) | ((j & 2) << 1) | ((j & 4) >> 1);
+  return kKPT * j;
+}
+
+// A workgroup-uniform value read through the scalar unit (the page table,
+// page->chunk table and chunk scales are not written while the kernel runs),
+// so that waiting for it does not also wait for the vector loads in flight.
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 // Per-page facts, uniform over the workgroup.
 // (32-bit fields only: a struct with padding bytes is copied through scratch
 // memory when the pipeline rotates it.)
@@ -106,22 +136,22 @@ __device__ __forceinline__ PageInfo page_info(const KvGeom& g, int64_t n_phys,
                                               int last_tokens, const PageInfo& prev,
                                               bool has_prev) {
   PageInfo p;
-  const int32_t lp = pages[pi];
+  const int32_t lp = load_uniform(pages + pi);
   bool mapped = lp >= 0 && lp < g.max_pages;
-  const int64_t phys = mapped ? (int64_t)g.page_table[lp] : -1;
+  const int64_t phys = mapped ? (int64_t)load_uniform(g.page_table + lp) : -1;
   mapped = mapped && phys >= 0 && phys < n_phys;
   p.mapped = mapped;
   p.page = g.pool + (mapped ? phys : 0) * g.page_bytes;
   p.valid = !mapped ? 0 : (pi == n_pages - 1 ? last_tokens : g.page_tokens);
-  int c0 = mapped ? g.page_chunk[2 * lp] : 0;
-  p.split = mapped ? g.page_chunk[2 * lp + 1] : g.page_tokens;
+  int c0 = mapped ? load_uniform(g.page_chunk + 2 * lp) : 0;
+  p.split = mapped ? load_uniform(g.page_chunk + 2 * lp + 1) : g.page_tokens;
   c0 = c0 < 0 ? 0 : (c0 >= g.max_chunks ? g.max_chunks - 1 : c0);
   p.c0 = c0;
   p.c1 = c0 + 1 < g.max_chunks ? c0 + 1 : g.max_chunks - 1;
-  p.sgk0 = g.k_gscale[p.c0];
-  p.sgk1 = g.k_gscale[p.c1];
-  p.sgv0 = g.v_gscale[p.c0];
-  p.sgv1 = g.v_gscale[p.c1];
+  p.sgk0 = load_uniform(g.k_gscale + p.c0);
+  p.sgk1 = load_uniform(g.k_gscale + p.c1);
+  p.sgv0 = load_uniform(g.v_gscale + p.c0);
+  p.sgv1 = load_uniform(g.v_gscale + p.c1);
   if (has_prev && prev.sgv0 == p.sgv0 && prev.sgv1 == p.sgv1)
     p.vcheck = prev.vcheck;
   else
@@ -132,12 +162,14 @@ __device__ __forceinline__ PageInfo page_info(const KvGeom& g, int64_t n_phys,
 // The raw inputs of one block for this thread: with G = kD / 8 channel groups
 // per key, its units are the kKPT adjacent keys kKPT (tid / G) + i in channel
 // group tid % G (the same 8 channels for every unit), written to V^T as
-// kKPT-key runs.  The K means of the page's two chunks (2 x kD floats) travel
-// one per thread and are shared through LDS.
+// kKPT-key runs.  The K means of those 8 channels, for the chunk of the
+// block's first slot, travel with them (the only chunk of a block that needs
+// no per-key choice; the other blocks read theirs when they are decoded), so
+// a block's decode waits only for loads issued one block earlier.
 template <int kKPT>
 struct BlockRaw {
   uint32_t kc[kKPT], ks[kKPT], vc[kKPT], vs[kKPT];
-  float mu;               // K mean of chunk (tid < kD ? c0 : c1), channel tid % kD (tid < 2 kD)
+  f32x4 mu_lo, mu_hi;     // K means of channels 8 (tid % G) + 0..3 and + 4..7
 };
 
 template <int kD>
@@ -149,7 +181,7 @@ __device__ __forceinline__ void fetch_block(const KvGeom& g, const PageInfo& p, 
   const uint32_t codes_region = H * P * (kD / 2);
   const uint32_t scales_region = H * P * (kD / 16);
   const uint32_t sub = threadIdx.x % kGroups;
-  const uint32_t row0 = (uint32_t)h * P + s0 + kKPT * (threadIdx.x / kGroups);
+  const uint32_t row0 = (uint32_t)h * P + s0 + unit_key0<kKPT, kGroups>();
 #pragma unroll
   for (int i = 0; i < kKPT; ++i) {
     const uint32_t row = row0 + i;
@@ -158,8 +190,9 @@ __device__ __forceinline__ void fetch_block(const KvGeom& g, const PageInfo& p, 
     r.vc[i] = *(const uint32_t*)(p.page + (codes_region + scales_region + row * (kD / 2) + 4 * sub));
     r.vs[i] = p.page[2 * codes_region + scales_region + row * (kD / 16) + (sub >> 1)];
   }
-  if (threadIdx.x < 2 * kD)
-    r.mu = g.k_mean[((int64_t)(threadIdx.x < kD ? p.c0 : p.c1) * H + h) * kD + (threadIdx.x & (kD - 1))];
+  const float* mp = g.k_mean + ((int64_t)(s0 >= p.split ? p.c1 : p.c0) * H + h) * kD + 8 * sub;
+  r.mu_lo = *(const f32x4*)mp;
+  r.mu_hi = *(const f32x4*)(mp + 4);
 }
 
 // Decode a fetched block into K^ rows and V^T columns of LDS.  Slots that hold
@@ -168,20 +201,27 @@ __device__ __forceinline__ void fetch_block(const KvGeom& g, const PageInfo& p, 
 // kSimple: the block is mapped, every slot holds a key and all belong to chunk
 // `cs` (uniform), so no per-key choice of chunk or mask is needed.
 template <int kD, bool kVCheck, bool kSimple>
-__device__ __forceinline__ void decode_block(const PageInfo& p, int s0, int cs,
-                                             const BlockRaw<Shape<kD>::kKPT>& r,
-                                             const float* __restrict__ Mu,
+__device__ __forceinline__ void decode_block(const KvGeom& g, int h, const PageInfo& p, int s0,
+                                             int cs, const BlockRaw<Shape<kD>::kKPT>& r,
                                              uint16_t* __restrict__ Ks,
                                              uint16_t* __restrict__ Vt) {
   constexpr int kKPT = Shape<kD>::kKPT, kGroups = Shape<kD>::kGroups;
   constexpr int kKsRow = Shape<kD>::kKsRow;
   const int sub = threadIdx.x % kGroups;
-  const float* m0p = Mu + (kSimple ? cs * kD : 0) + 8 * sub;
-  const f32x4 a0 = *(const f32x4*)m0p, b0 = *(const f32x4*)(m0p + 4);
+  // K means: the fetched ones (chunk cs) for a simple block; both chunks'
+  // from memory otherwise (chunk boundaries, unmapped or partial pages)
+  f32x4 a0 = r.mu_lo, b0 = r.mu_hi, a1, b1;
+  if (!kSimple) {
+    const float* m0p = g.k_mean + ((int64_t)p.c0 * g.n_heads + h) * kD + 8 * sub;
+    const float* m1p = g.k_mean + ((int64_t)p.c1 * g.n_heads + h) * kD + 8 * sub;
+    a0 = *(const f32x4*)m0p;
+    b0 = *(const f32x4*)(m0p + 4);
+    a1 = *(const f32x4*)m1p;
+    b1 = *(const f32x4*)(m1p + 4);
+  }
   const float mu0[8] = {a0[0], a0[1], a0[2], a0[3], b0[0], b0[1], b0[2], b0[3]};
   float mu1[8];
   if (!kSimple) {
-    const f32x4 a1 = *(const f32x4*)(Mu + kD + 8 * sub), b1 = *(const f32x4*)(Mu + kD + 8 * sub + 4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       mu1[e] = a1[e];
@@ -192,7 +232,7 @@ __device__ __forceinline__ void decode_block(const PageInfo& p, int s0, int cs,
   uint32_t vw[kKPT][4];                                     // V^ words of the thread's keys
 #pragma unroll
   for (int i = 0; i < kKPT; ++i) {
-    const int key = kKPT * (threadIdx.x / kGroups) + i;
+    const int key = unit_key0<kKPT, kGroups>() + i;
     u32x4 ko, vo;
     if (kSimple) {
       kv_unit_bf16<kVCheck>(r.kc[i], r.ks[i], r.vc[i], r.vs[i], sgk_s, sgv_s, mu0, ko, vo);
@@ -211,11 +251,12 @@ __device__ __forceinline__ void decode_block(const PageInfo& p, int s0, int cs,
   }
   // V^T row 8 sub + c holds channel c of the keys: bf16 of key i is the low
   // (c even) or high (c odd) half of vw[i][c / 2].  Keys sit at position
-  // vt_pos(key) of the row (runs of 4 keys stay contiguous).
-  const int k0 = vt_pos(kKPT * (threadIdx.x / kGroups));
+  // vt_pos(key) of the row (runs of 4 keys stay contiguous), stored at
+  // vt_index (the same chunk permutation for the 8 rows of this thread).
+  const int k0 = vt_pos(unit_key0<kKPT, kGroups>());
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    uint16_t* vt = Vt + (8 * sub + c) * kVtRow + k0;
+    uint16_t* vt = Vt + vt_index(8 * sub + c, k0);
     if (kKPT == 1) {
       *vt = (uint16_t)((c & 1) ? vw[0][c >> 1] >> 16 : vw[0][c >> 1]);
       continue;
@@ -359,6 +400,10 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ Kc,
 
   // O^T += V^T P^T.  Step kk of key tile kt: k index j of lane half `half` is
   // key 32 kt + 16 kk + (j / 4) * 8 + 4 half + j % 4 = S^T register 8 kk + j.
+  // Lane reads row 32 dt + lane % 32 at position 32 kt + 16 kk + 8 half, i.e.
+  // vt_index: chunk (4 kt + 2 kk + half) ^ (2 dt + lane / 16 % 2), split into
+  // a per-lane part (bit 0) and a compile-time part.
+  const uint16_t* vrow = Vc + (lane & 31) * kVtRow + 8 * (half ^ ((lane >> 4) & 1));
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -369,7 +414,7 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ Kc,
 #pragma unroll
       for (int dt = 0; dt < kD / 32; ++dt) {
         // the 8 keys of this lane half are contiguous in the V^T row (vt_pos)
-        const uint16_t* vp = Vc + (32 * dt + (lane & 31)) * kVtRow + 32 * kt + 16 * kk + 8 * half;
+        const uint16_t* vp = vrow + 32 * dt * kVtRow + 8 * ((4 * kt + 2 * kk) ^ (2 * dt));
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*(const u32x4*)vp),
                                                         as_bf16x8(pb), o[dt], 0, 0, 0);
       }
@@ -377,22 +422,20 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ Kc,
   }
 }
 
-// Decode block (page facts p, first slot s0, raw inputs r) into (Kn, Vn) with
-// the K means in Mu.
+// Decode block (page facts p, first slot s0, raw inputs r) of head h into (Kn, Vn).
 template <int kD>
-__device__ __forceinline__ void decode_any(const PageInfo& p, int s0,
+__device__ __forceinline__ void decode_any(const KvGeom& g, int h, const PageInfo& p, int s0,
                                            const BlockRaw<Shape<kD>::kKPT>& r,
-                                           const float* __restrict__ Mu,
                                            uint16_t* __restrict__ Kn, uint16_t* __restrict__ Vn) {
   const bool one_chunk = s0 + kKB <= p.split || s0 >= p.split;
   const bool simple = p.mapped && s0 + kKB <= p.valid && one_chunk;
   const int cs = s0 >= p.split ? 1 : 0;
   if (simple) {
-    if (p.vcheck) decode_block<kD, true, true>(p, s0, cs, r, Mu, Kn, Vn);
-    else decode_block<kD, false, true>(p, s0, cs, r, Mu, Kn, Vn);
+    if (p.vcheck) decode_block<kD, true, true>(g, h, p, s0, cs, r, Kn, Vn);
+    else decode_block<kD, false, true>(g, h, p, s0, cs, r, Kn, Vn);
   } else {
-    if (p.vcheck) decode_block<kD, true, false>(p, s0, 0, r, Mu, Kn, Vn);
-    else decode_block<kD, false, false>(p, s0, 0, r, Mu, Kn, Vn);
+    if (p.vcheck) decode_block<kD, true, false>(g, h, p, s0, 0, r, Kn, Vn);
+    else decode_block<kD, false, false>(g, h, p, s0, 0, r, Kn, Vn);
   }
 }
 
@@ -412,13 +455,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                                                            uint32_t q_sign,
                                                            uint16_t* __restrict__ out,
                                                            float* __restrict__ part, int n_split) {
-  // LDS (Shape<kD>::kLds bytes, dynamic): K^ rows, V^T rows, K means of chunk c0 then c1
+  // LDS (Shape<kD>::kLds bytes, dynamic): K^ rows, V^T rows
   constexpr int kKsRow = Shape<kD>::kKsRow;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   constexpr size_t kKsElems = Shape<kD>::kKsElems, kVtElems = Shape<kD>::kVtElems;
   uint16_t* Kb = smem;                                    // buffer i at Kb + i kKsElems
   uint16_t* Vb = Kb + 2 * kKsElems;                       // buffer i at Vb + i kVtElems
-  float* Mb = (float*)(Vb + 2 * kVtElems);                // buffer i at Mb + i 2 kD
   const int H = g.n_heads, P = g.page_tokens;
   const int h = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -451,26 +493,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int nb = n_pages * bpp;
   const int b0 = (int)((int64_t)nb * split / n_split), b1 = (int)((int64_t)nb * (split + 1) / n_split);
 
-  // Pipeline: on entry to iteration b, buffer b & 1 holds decoded block b, the
-  // raw inputs of block b + 1 are in flight (rn) and Mu buffer (b + 1) & 1
-  // holds its K means.  Iteration b multiplies block b and, between its S^T
-  // MFMAs and its softmax, decodes block b + 1 and then reuses rn to fetch
-  // block b + 2; one barrier ends it.
+  // Pipeline: on entry to iteration b, buffer b & 1 holds decoded block b and
+  // the raw inputs of block b + 1 (with their K means) are in flight (rn).
+  // Iteration b multiplies block b and, between its S^T MFMAs and its softmax,
+  // decodes block b + 1 and then reuses rn to fetch block b + 2; one barrier
+  // ends it, and nothing before that barrier waits for the fetch.
   if (b0 < b1) {
     PageInfo pc;
     pc = page_info(g, n_phys, pages, b0 / bpp, n_pages, last_tokens, pc, false);
     BlockRaw<Shape<kD>::kKPT> rn;
     fetch_block<kD>(g, pc, h, (b0 % bpp) * kKB, rn);
-    if (tid < 2 * kD) Mb[(b0 & 1) * 2 * kD + tid] = rn.mu;
-    __syncthreads();
-    decode_any<kD>(pc, (b0 % bpp) * kKB, rn, Mb + (b0 & 1) * 2 * kD, Kb + (b0 & 1) * kKsElems,
+    decode_any<kD>(g, h, pc, (b0 % bpp) * kKB, rn, Kb + (b0 & 1) * kKsElems,
                    Vb + (b0 & 1) * kVtElems);
     PageInfo pn = pc;
     if (b0 + 1 < b1) {
       if ((b0 + 1) % bpp == 0)
         pn = page_info(g, n_phys, pages, (b0 + 1) / bpp, n_pages, last_tokens, pc, true);
       fetch_block<kD>(g, pn, h, ((b0 + 1) % bpp) * kKB, rn);
-      if (tid < 2 * kD) Mb[((b0 + 1) & 1) * 2 * kD + tid] = rn.mu;
     }
     __syncthreads();
 
@@ -483,7 +522,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         pn2 = page_info(g, n_phys, pages, (b + 2) / bpp, n_pages, last_tokens, pn, true);
       const auto decode_next = [&]() {
         if (has1) {
-          decode_any<kD>(pn, ((b + 1) % bpp) * kKB, rn, Mb + nxt * 2 * kD, Kb + nxt * kKsElems,
+          decode_any<kD>(g, h, pn, ((b + 1) % bpp) * kKB, rn, Kb + nxt * kKsElems,
                          Vb + nxt * kVtElems);
           if (has2) fetch_block<kD>(g, pn2, h, ((b + 2) % bpp) * kKB, rn);
         }
@@ -495,8 +534,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                          scale_log2e, m, l, o, decode_next);
       else
         decode_next();
-      // K means of block b + 2 into the Mu buffer that block b's decode used
-      if (has2 && tid < 2 * kD) Mb[cur * 2 * kD + tid] = rn.mu;
       __syncthreads();
       pc = pn;
       pn = pn2;
