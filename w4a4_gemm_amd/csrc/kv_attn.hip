@@ -86,11 +86,11 @@ __device__ __forceinline__ int vt_pos(int k) {
 // Offset (bf16) of position pos of V^T row `row` in a V^T buffer: the
 // row's 16-byte chunks are permuted, chunk pos / 8 stored at chunk
 // (pos / 8) ^ ((row / 16) % 8).  A decode write instruction covers rows
-// 8 u + c of the 16 channel groups u and, with unit_key0's key order, all
-// four dwords of one chunk: the permutation puts its 64 dwords in 64
-// distinct LDS banks (rows 8 apart alone would share 8).  The O^T reads
-// (16 lanes = 16 consecutive rows, one chunk) stay conflict-free: the 16
-// rows share one permutation.
+// 8 u + c of the 16 channel groups u, which without the permutation share a
+// few LDS banks: measured on the device, a transposed write instruction
+// takes 64 LDS cycles with plain rows and 8 with the permutation and
+// unit_key0's key order, while the O^T fragment reads go from 4 to 8 cycles
+// (a two-way conflict): 1.9 K against 0.6 K conflict cycles per block.
 __device__ __forceinline__ int vt_index(int row, int pos) {
   return row * kVtRow + 8 * ((pos >> 3) ^ ((row >> 4) & 7)) + (pos & 7);
 }
