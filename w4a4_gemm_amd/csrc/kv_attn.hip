@@ -462,10 +462,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   uint16_t* Kb = smem;                                    // buffer i at Kb + i kKsElems
   uint16_t* Vb = Kb + 2 * kKsElems;                       // buffer i at Vb + i kVtElems
   const int H = g.n_heads, P = g.page_tokens;
-  const int h = blockIdx.y, split = blockIdx.z;
+  // Work order: the (head, split) pairs of query block 0, then of block 1, ...
+  // so the last query block, the one that may be partial and then runs faster,
+  // is dispatched last and fills the tail; the query blocks of one (head,
+  // split), which read the same pages, are heads x splits workgroups apart,
+  // on one XCD when that count is a multiple of 8.
+  const int n_hs = (int)(gridDim.y * gridDim.z);
+  const int wg = (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+  const int qblk = wg / n_hs, hs = wg % n_hs;
+  const int h = hs % (int)gridDim.y, split = hs / (int)gridDim.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5;
-  const int64_t wave_q0 = (int64_t)blockIdx.x * kQB + wave * 32;   // the wave's first query
+  const int64_t wave_q0 = (int64_t)qblk * kQB + wave * 32;   // the wave's first query
   const int64_t qrow = wave_q0 + (lane & 31);
 
   // The lane's query row in registers, as the B operand of S^T = K^ Q^T:
