@@ -578,8 +578,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 // Merge the splits of one (query, head) row: M = max m_s, L = sum l_s 2^(m_s - M),
 // O = sum O_s 2^(m_s - M) / L, rounded once to bf16.  One wave per row, kD / 64
-// channels per lane.  Splits are read kChunk at a time with all their loads in
-// flight; the sums still run over s in increasing order.
+// channels per lane.  Up to kChunk splits are read in one round of loads (m, l
+// and O together); more splits take a first pass for M and then kChunk at a
+// time with all their loads in flight.  The sums run over s in increasing
+// order either way.
 template <int kD>
 __global__ __launch_bounds__(256) void kv_attention_combine(const float* __restrict__ part,
                                                             int n_split, int64_t rows,
@@ -591,6 +593,40 @@ __global__ __launch_bounds__(256) void kv_attention_combine(const float* __restr
   if (row >= rows) return;
   const float* ml = part + (int64_t)n_split * rows * kD;
   float M = -__builtin_inff();
+  if (n_split <= kChunk) {
+    f32x2 v[kChunk];
+    float ov[kChunk][kCpl];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      v[i] = f32x2{-__builtin_inff(), 0.0f};
+      if (i < n_split) {
+        v[i] = *(const f32x2*)(ml + ((int64_t)i * rows + row) * 2);
+        const float* os = part + ((int64_t)i * rows + row) * kD + kCpl * lane;
+#pragma unroll
+        for (int c = 0; c < kCpl; ++c) ov[i][c] = os[c];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) M = fmaxf(M, v[i][0]);
+    float L = 0.0f, a[kCpl] = {};
+    if (M != -__builtin_inff()) {
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        if (i < n_split) {
+          const float w = __builtin_amdgcn_exp2f(v[i][0] - M);   // 0 for an empty split (m = -inf)
+          L += v[i][1] * w;
+#pragma unroll
+          for (int c = 0; c < kCpl; ++c) a[c] += ov[i][c] * w;
+        }
+      }
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    if (kCpl == 2)
+      *(uint32_t*)(out + row * kD + 2 * lane) = pack_bf16x2(a[0] * inv, a[kCpl - 1] * inv);
+    else
+      out[row * kD + lane] = (uint16_t)f32_to_bf16_bits(a[0] * inv);
+    return;
+  }
   for (int s0 = 0; s0 < n_split; s0 += kChunk) {
     float mv[kChunk];
 #pragma unroll
