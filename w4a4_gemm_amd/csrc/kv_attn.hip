@@ -83,27 +83,34 @@ __device__ __forceinline__ int vt_pos(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
-// Offset (bf16) of position pos of V^T row `row` in a V^T buffer: the
+// Offset (bf16) of channel ch's V^T row at key position pos in a V^T buffer.
+// The row of channel ch is ch with bit 0 flipped when bit 4 is set, and the
 // row's 16-byte chunks are permuted, chunk pos / 8 stored at chunk
-// (pos / 8) ^ ((row / 16) % 8).  A decode write instruction covers rows
-// 8 u + c of the 16 channel groups u, which without the permutation share a
-// few LDS banks: measured on the device, a transposed write instruction
-// takes 64 LDS cycles with plain rows and 8 with the permutation and
-// unit_key0's key order, while the O^T fragment reads go from 4 to 8 cycles
-// (a two-way conflict): 1.9 K against 0.6 K conflict cycles per block.
-__device__ __forceinline__ int vt_index(int row, int pos) {
-  return row * kVtRow + 8 * ((pos >> 3) ^ ((row >> 4) & 7)) + (pos & 7);
+// (pos / 8) ^ (2 ((ch / 32) % 4)).  A decode write instruction covers the
+// rows of channel c of the 16 channel groups (8 apart, so without a
+// permutation they share a few LDS banks) and, with unit_key0's key order,
+// four dwords of one chunk; these two permutations spread them over all
+// banks, while the O^T fragment reads (32 rows of one 32-channel block, one
+// chunk) keep their conflict-free pattern.  Measured on the device: a
+// transposed write instruction takes 2 LDS cycles (64 with plain rows) and a
+// fragment read 4, neither with bank conflicts.
+__device__ __forceinline__ int vt_index(int ch, int pos) {
+  return (ch ^ ((ch >> 4) & 1)) * kVtRow + 8 * ((pos >> 3) ^ (2 * ((ch >> 5) & 3))) + (pos & 7);
 }
 
 // First key of this thread's decode units (kKPT adjacent keys; kGroups =
-// kD / 8 threads share a key run).  With two keys per thread the index of
-// the pair has bits 1 and 2 swapped, so that the four pairs of a wave are
-// keys {0, 2, 8, 10} + 4 (bit 0 of the wave) + 16 m: vt_pos makes them one
-// 16-byte chunk of each V^T row.
+// kD / 8 threads share a key run).  With two keys per thread the wave's four
+// key pairs are keys {0, 2, 8, 10} + 4 (bit 0 of the wave) + 16 m, i.e. the
+// four dwords of one V^T chunk (the pair index has bits 1 and 2 swapped), and
+// a thread of odd channel group takes the pair of the other half of the wave
+// (slot XOR 2), so that each 32-lane half of a write covers all four dwords.
 template <int kKPT, int kGroups>
 __device__ __forceinline__ int unit_key0() {
   int j = (int)threadIdx.x / kGroups;
-  if (kKPT == 2) j = (j & ~6) | ((j & 2) << 1) | ((j & 4) >> 1);
+  if (kKPT == 2) {
+    j = (j & ~3) | ((j & 3) ^ (2 * ((int)(threadIdx.x % kGroups) & 1)));
+    j = (j & ~6) | ((j & 2) << 1) | ((j & 4) >> 1);
+  }
   return kKPT * j;
 }
 
@@ -249,14 +256,19 @@ __device__ __forceinline__ void decode_block(const KvGeom& g, int h, const PageI
 #pragma unroll
     for (int e = 0; e < 4; ++e) vw[i][e] = vo[e];
   }
-  // V^T row 8 sub + c holds channel c of the keys: bf16 of key i is the low
-  // (c even) or high (c odd) half of vw[i][c / 2].  Keys sit at position
-  // vt_pos(key) of the row (runs of 4 keys stay contiguous), stored at
-  // vt_index (the same chunk permutation for the 8 rows of this thread).
+  // Channel 8 sub + c: bf16 of key i is the low (c even) or high (c odd)
+  // half of vw[i][c / 2].  Keys sit at position vt_pos(key) of the row (runs
+  // of 4 keys stay contiguous), stored at vt_index: for this thread's
+  // channels the chunk permutation is one constant and the row is 8 sub + c
+  // moved by +b (c even) or -b (c odd), b = bit 1 of sub.
   const int k0 = vt_pos(unit_key0<kKPT, kGroups>());
+  const int vb = (sub >> 1) & 1;
+  uint16_t* const vt0 = Vt + (8 * sub) * kVtRow + 8 * ((k0 >> 3) ^ (2 * ((sub >> 2) & 3))) + (k0 & 7);
+  uint16_t* const vt_even = vt0 + vb * kVtRow;
+  uint16_t* const vt_odd = vt0 - vb * kVtRow;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    uint16_t* vt = Vt + vt_index(8 * sub + c, k0);
+    uint16_t* vt = ((c & 1) ? vt_odd : vt_even) + c * kVtRow;
     if (kKPT == 1) {
       *vt = (uint16_t)((c & 1) ? vw[0][c >> 1] >> 16 : vw[0][c >> 1]);
       continue;
@@ -400,10 +412,11 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ Kc,
 
   // O^T += V^T P^T.  Step kk of key tile kt: k index j of lane half `half` is
   // key 32 kt + 16 kk + (j / 4) * 8 + 4 half + j % 4 = S^T register 8 kk + j.
-  // Lane reads row 32 dt + lane % 32 at position 32 kt + 16 kk + 8 half, i.e.
-  // vt_index: chunk (4 kt + 2 kk + half) ^ (2 dt + lane / 16 % 2), split into
-  // a per-lane part (bit 0) and a compile-time part.
-  const uint16_t* vrow = Vc + (lane & 31) * kVtRow + 8 * (half ^ ((lane >> 4) & 1));
+  // Lane reads channel 32 dt + x (x = lane % 32) at position 32 kt + 16 kk +
+  // 8 half, i.e. vt_index: row 32 dt + (x with bit 0 flipped when bit 4 is
+  // set), chunk ((4 kt + 2 kk) ^ 2 dt) + half.
+  const int vx = lane & 31;
+  const uint16_t* vrow = Vc + (vx ^ ((vx >> 4) & 1)) * kVtRow + 8 * half;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
