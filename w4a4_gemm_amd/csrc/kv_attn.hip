@@ -167,7 +167,7 @@ __device__ __forceinline__ PageInfo page_info(const KvGeom& g, int64_t n_phys,
 }
 
 // The raw inputs of one block for this thread: with G = kD / 8 channel groups
-// per key, its units are the kKPT adjacent keys kKPT (tid / G) + i in channel
+// per key, its units are the kKPT adjacent keys unit_key0() + i in channel
 // group tid % G (the same 8 channels for every unit), written to V^T as
 // kKPT-key runs.  The K means of those 8 channels, for the chunk of the
 // block's first slot, travel with them (the only chunk of a block that needs
