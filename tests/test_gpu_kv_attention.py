@@ -183,6 +183,26 @@ def test_head_dim_64_two_chunks_ragged_queries():
     _check(gpu, ora, [3, 1, 0], p, qb, 0.2, 8)
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_many_splits_merge(d):
+    # one query block of 2 heads over 160 shuffled pages: the window is split
+    # more than 8 ways, so the merge reads its splits in several rounds after
+    # a first pass for the maxima; a chunk boundary falls inside a block
+    h, p, n_pages, n_q = 2, 64, 160, 40
+    table = synth.page_permutation(n_pages, 111)[None, :]
+    gpu, ora = _pair(h, p, n_pages, 2, table, n_pages, d=d)
+    ws = nv.nvfp4_workspace_bytes(nv.OP_KV_ATTENTION, n_q, h, n_pages * p)
+    splits = ws // (n_q * h * (128 + 2) * 4)
+    assert splits > 8, splits
+    kb, vb = synth.kv_chunk(t=n_pages * p, h=h, d=d, seed_k=112, seed_v=113, seed_off=114)
+    cut = n_pages * p // 2 + 32
+    _write(gpu, ora, 0, kb[:cut], vb[:cut], 0)
+    _write(gpu, ora, 1, kb[cut:], vb[cut:], cut)
+    qb = synth.attn_queries(n_q, h, d, seed=115)
+    order = [int(x) for x in synth.page_permutation(n_pages, 116)]
+    _check(gpu, ora, order, p, qb, 1 / math.sqrt(d), n_pages)
+
+
 def test_head_dim_64_split_window():
     # a one-block query grid over 24 pages: the window is split over workgroups
     # and merged by the combine kernel (one channel per lane at head_dim 64)
