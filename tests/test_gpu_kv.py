@@ -149,6 +149,39 @@ def test_k_mean_exact_full_chunk_with_tiny_values():
     _compare_dequant(gpu, ora, 0, [0, 5, 27])
 
 
+def _midpoint_significands(g):
+    """How many of the 16 significands a of q s_b ({1, 1.5} x (1 + m/8)) give
+    RN32(a g) exactly on a bf16 midpoint while a g itself is not (fp64 holds
+    a g exactly): for such a scale the V^ decode needs its exact fix-up."""
+    g = np.float32(g)
+    n = 0
+    for i in range(16):
+        a = (1.5 if i & 8 else 1.0) * (1.0 + (i & 7) * 0.125)
+        pf = np.float32(np.float64(a) * np.float64(g))
+        if (int(pf.view(np.uint32)) & 0xFFFF) == 0x8000 and np.float64(pf) != a * np.float64(g):
+            n += 1
+    return n
+
+
+def test_v_products_on_bf16_midpoints():
+    # max|V| = 1.0390625 gives s_gV = RN32(1.0390625 / 2688), for which some
+    # products q s_b s_gV round (in fp32) onto a bf16 midpoint: the window read
+    # must still give V^ = RN_bf16(q s_b s_gV) with one rounding
+    h, d, p = 2, 128, 64
+    table = np.arange(12, dtype=np.int32)[None, :]
+    gpu, ora = _pair(1, h, d, p, 12, 1, table, 12)
+    kb, vb = synth.kv_chunk(t=12 * p, h=h, d=d, seed_k=120, seed_v=121, seed_off=122)
+    v = F.bf16_bits_to_f64(vb)
+    v = v * 2.0 ** -int(np.ceil(np.log2(np.max(np.abs(v)) + 1e-30)))   # |v| <= 1, exact
+    v.flat[5] = 1.0390625
+    _write(gpu, ora, 0, 0, kb, F.f64_to_bf16_bits(v), 0)
+    _compare_state(gpu, ora, 0, [0], list(range(12)))
+    sgv = float(ora.v_gscale[0, 0])
+    assert _midpoint_significands(sgv) > 0, sgv
+    _compare_dequant(gpu, ora, 0, list(range(12)))
+    _compare_dequant(gpu, ora, 0, [11, 3, 0, 7])
+
+
 def test_invalid_listed_pages_give_zeros():
     h, d, p = 2, 64, 32
     gpu, ora = _pair(1, h, d, p, 4, 1, np.array([[0, 1, 2, 3]], np.int32), 4)

@@ -203,6 +203,21 @@ def test_many_splits_merge(d):
     _check(gpu, ora, order, p, qb, 1 / math.sqrt(d), n_pages)
 
 
+def test_v_scale_with_midpoint_products():
+    # max|V| = 1.0390625: products q s_b s_gV round (in fp32) onto bf16
+    # midpoints, so every page takes the V decode with the exact fix-up
+    h, p = 2, 64
+    table = np.arange(12, dtype=np.int32)[None, :]
+    gpu, ora = _pair(h, p, 12, 1, table, 12)
+    kb, vb = synth.kv_chunk(t=12 * p, h=h, d=128, seed_k=120, seed_v=121, seed_off=122)
+    v = F.bf16_bits_to_f64(vb)
+    v = v * 2.0 ** -int(np.ceil(np.log2(np.max(np.abs(v)) + 1e-30)))   # |v| <= 1, exact
+    v.flat[5] = 1.0390625
+    _write(gpu, ora, 0, kb, F.f64_to_bf16_bits(v), 0)
+    qb = synth.attn_queries(70, h, 128, seed=123)
+    _check(gpu, ora, list(range(12)), p, qb, 1 / math.sqrt(128), 12)
+
+
 def test_head_dim_64_split_window():
     # a one-block query grid over 24 pages: the window is split over workgroups
     # and merged by the combine kernel (one channel per lane at head_dim 64)
