@@ -123,6 +123,32 @@ def test_row_stride_mixed_whole_and_edge_tiles(dtype):
     assert float(am.cpu()[0]) == float(np.max(np.abs(y)))
 
 
+def test_output_beyond_4gib():
+    """Y of 70000 x 32768 bf16 (4.6 GB, 65536 bytes per row): whole wave tiles and
+    the ragged last tile row at byte offsets past 2^31 and 2^32, max|Y| folded over
+    all of them; sampled outputs, with the last row and column, against exact dot
+    products."""
+    rng = np.random.default_rng(21)
+    m, n, k = 70000, 32768, 64
+    xq = Q.quantize(rng.standard_normal((m, k)))
+    wq = Q.quantize(rng.standard_normal((n, k)) * 0.02)
+    am = torch.zeros(1, dtype=torch.float32, device=dev())
+    y = nv.nvfp4_gemm_w4a4(from_oracle(xq, nv.SCALES_ROWMAJOR), from_oracle(wq, nv.SCALES_TILED),
+                           torch.bfloat16, y_amax=am)
+    rows = rng.integers(0, m, 3000)
+    cols = rng.integers(0, n, 3000)
+    rows[:8] = [m - 1, m - 1, 32767, 32768, 65535, 65536, 69887, 69888]
+    cols[:8] = [n - 1, 0, n - 1, 0, 255, 256, n - 1, 0]
+    got = y[torch.from_numpy(rows).to(dev()), torch.from_numpy(cols).to(dev())]
+    ymax = float(y.abs().amax().float().cpu())
+    got = got.float().cpu().numpy().astype(np.float64)
+    del y
+    y_ref, a_ref = Q.gemm_pairs(xq, wq, rows, cols)
+    ok, n_clause, n_fail = Q.check_gemm_bf16(got, y_ref, a_ref)
+    assert ok, (n_clause, n_fail)
+    assert float(am.cpu()[0]) == ymax
+
+
 def test_empty_k_gives_zeros():
     """K == 0: the sum over k is empty, so Y = 0 (and max|Y| = 0)."""
     xq = Q.quantize(np.zeros((70, 0)))

@@ -229,3 +229,35 @@ def test_head_dim_64_split_window():
     _write(gpu, ora, 0, kb, vb, 0)
     qb = synth.attn_queries(40, h, d, seed=110)
     _check(gpu, ora, list(range(24)), p, qb, 1 / math.sqrt(d), 24)
+
+
+def test_pages_beyond_4gib():
+    """A 4.4 GB pool (5000 pages of 24 heads x 256 tokens, 885 KB each) whose listed
+    pages lie past 2^31 and 2^32 bytes, two of them straddling those offsets: the
+    written bytes and the window read are bit-exact and the attention is within the
+    tolerance.  The oracle keeps a small pool of its own: where a page is placed
+    changes no value."""
+    h, d, p = 24, 128, 256
+    n_phys = 5000
+    gtab = np.array([[4999, 2427, 4860, 0, 4998, 4854]], dtype=np.int32)
+    gpu = nv.KVCache(1, h, d, p, 6, 2, gtab, n_phys, device=dev())
+    ora = KV.KVPool(1, h, d, p, 6, 2, np.arange(6, dtype=np.int32)[None, :], 6)
+    pb = gpu.page_bytes
+    assert 2427 * pb < 2 ** 31 < 2428 * pb and 4854 * pb < 2 ** 32 < 4855 * pb
+    kb, vb = synth.kv_chunk(t=1400, h=h, d=d, seed_k=124, seed_v=125, seed_off=126)
+    _write(gpu, ora, 0, kb[:700], vb[:700], 0)
+    _write(gpu, ora, 1, kb[700:], vb[700:], 700)              # pages 2 (from slot 188) .. 5
+    torch.cuda.synchronize()
+    for lp in range(6):
+        g = gpu.pool[int(gtab[0, lp])].cpu().numpy()
+        assert np.array_equal(g, ora.pool[lp]), f"page {lp}: {np.sum(g != ora.pool[lp])} bytes"
+    pages = [3, 5, 0, 4, 1, 2]
+    lp = torch.tensor(pages, dtype=torch.int32, device=dev())
+    kh, vh = nv.nvfp4_kv_dequant_blocks(gpu, 0, lp)
+    torch.cuda.synchronize()
+    ko, vo = ora.dequant_pages(0, pages)
+    assert np.array_equal(kh.float().cpu().numpy().astype(np.float64), ko)
+    assert np.array_equal(vh.float().cpu().numpy().astype(np.float64), vo)
+    qb = synth.attn_queries(300, h, d, seed=127)
+    order = [0, 1, 2, 3, 4, 5]
+    _check(gpu, ora, order, 1400 - 5 * p, qb, 1 / math.sqrt(d), 6)
