@@ -168,3 +168,29 @@ def test_full_size_attn_proj_activation():
     d = synth.attn_proj()
     x64 = F.bf16_bits_to_f64(d["x"])
     _quantize_and_compare(x64, bf16_tensor(d["x"]), nv.SCALES_TILED)
+
+
+@pytest.mark.slow
+def test_quantize_dequantize_beyond_4gib():
+    """98304 x 22528 bf16 (2.2 G values, 4.4 GB; value 2^30 lies in row 47662 and value
+    2^31 in row 95325): s_g from the amax pass over all of it, and the codes, scale
+    bytes (tiled) and bf16 dequantization (a 4.4 GB output) of four 128-row bands --
+    the first, those holding input byte offsets 2^31 and 2^32, the last -- bit-exact."""
+    m, n = 98304, 22528
+    bits = synth.to_bf16_bits(synth.normal_f32((m, n), 1.0, 41))
+    bits[m - 1, n - 1] = 0x4220                       # 40.0, the largest magnitude, last
+    amax = float(F.bf16_bits_to_f64(np.array([np.max(bits & 0x7FFF)], dtype=np.uint16))[0])
+    assert amax == 40.0
+    q = nv.nvfp4_quantize(bf16_tensor(bits), layout=nv.SCALES_TILED)
+    y = nv.nvfp4_dequantize(q, torch.bfloat16)
+    torch.cuda.synchronize()
+    s_g = float(q.global_scale.cpu()[0])
+    flat = q.scales.cpu().numpy()
+    for r0 in (0, 47616, 95232, m - 128):
+        band = Q.quantize(F.bf16_bits_to_f64(bits[r0:r0 + 128]), amax=amax)
+        assert s_g == band.s_g
+        r, kb = np.meshgrid(np.arange(r0, r0 + 128), np.arange(n // 16), indexing="ij")
+        assert np.array_equal(flat[Q.tiled_offset(r, kb, n)], band.scales), f"scales, band {r0}"
+        assert np.array_equal(q.codes[r0:r0 + 128].cpu().numpy(), band.packed), f"codes, band {r0}"
+        yb = y[r0:r0 + 128].float().cpu().numpy().astype(np.float64)
+        assert np.array_equal(yb, Q.dequantize(band, "bf16")), f"dequantized, band {r0}"
