@@ -80,6 +80,30 @@ def test_ragged_shapes(m, n, k):
     assert Q.check_gemm_bf16(yb, y_ref, a_ref)[0]
 
 
+def test_seeded_shape_sweep():
+    """32 seeded shapes: M, N in [1, 700], K a multiple of 16 up to 1200 (a quarter of the
+    cases with 128-row multiples and K % 64 == 0, so that the tiled scale layout is drawn
+    too), row scales spread over 2^-12 .. 2^12, bf16 or fp32 output."""
+    rng = np.random.default_rng(77)
+    for i in range(32):
+        m, n, k = int(rng.integers(1, 701)), int(rng.integers(1, 701)), 16 * int(rng.integers(1, 76))
+        if i % 4 == 0:
+            m, n, k = 128 * int(rng.integers(1, 6)), 128 * int(rng.integers(1, 6)), 64 * int(rng.integers(1, 19))
+        x = rng.standard_normal((m, k)) * np.exp2(rng.integers(-12, 13, (m, 1)))
+        w = rng.standard_normal((n, k)) * 0.02
+        xq, wq = _operands_from_f32(x.astype(np.float32), w.astype(np.float32))
+        lx = nv.SCALES_TILED if (m % 128 == 0 and k % 64 == 0 and rng.integers(2)) else nv.SCALES_ROWMAJOR
+        lw = nv.SCALES_TILED if (n % 128 == 0 and k % 64 == 0 and rng.integers(2)) else nv.SCALES_ROWMAJOR
+        dt = torch.bfloat16 if rng.integers(2) else torch.float32
+        print(f"[sweep {i}] M={m} N={n} K={k} layouts {lx}{lw} {dt}", flush=True)
+        y = _run(xq, wq, dt, lx, lw)
+        y_ref, a_ref = Q.gemm(xq, wq)
+        if dt == torch.float32:
+            assert Q.check_gemm_f32(y, y_ref, a_ref)[0], i
+        else:
+            assert Q.check_gemm_bf16(y, y_ref, a_ref)[0], i
+
+
 @pytest.mark.parametrize("m,n,k", [(96, 80, 16), (130, 70, 48), (257, 193, 80), (64, 300, 208),
                                    (40, 24, 1040)])
 def test_ragged_k(m, n, k):

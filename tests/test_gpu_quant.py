@@ -49,6 +49,26 @@ def test_ragged_rows_and_cols_rowmajor():
     _quantize_and_compare(x.astype(np.float64), f32_tensor(x), nv.SCALES_ROWMAJOR)
 
 
+def test_seeded_shape_sweep():
+    """24 seeded tensors: rows in [1, 600], cols a multiple of 16 up to 1600 (tiled layout
+    where rows % 128 == 0 and cols % 64 == 0), row magnitudes spread over 2^-20 .. 2^20,
+    fp32 or bf16 input, a third with the amax given; every byte bit-exact."""
+    rng = np.random.default_rng(78)
+    for i in range(24):
+        r, c = int(rng.integers(1, 601)), 16 * int(rng.integers(1, 101))
+        if i % 3 == 0:
+            r, c = 128 * int(rng.integers(1, 5)), 64 * int(rng.integers(1, 26))
+        x = (rng.standard_normal((r, c)) * np.exp2(rng.integers(-20, 21, (r, 1)))).astype(np.float32)
+        layout = nv.SCALES_TILED if (r % 128 == 0 and c % 64 == 0) else nv.SCALES_ROWMAJOR
+        amax = float(np.float32(np.max(np.abs(x)) * 1.5)) if i % 3 == 1 else None
+        print(f"[sweep {i}] {r} x {c} layout {layout} amax {amax}", flush=True)
+        if rng.integers(2):
+            bits = synth.to_bf16_bits(x)
+            _quantize_and_compare(F.bf16_bits_to_f64(bits), bf16_tensor(bits), layout, amax=amax)
+        else:
+            _quantize_and_compare(x.astype(np.float64), f32_tensor(x), layout, amax=amax)
+
+
 def test_strided_input():
     rng = np.random.default_rng(6)
     big = rng.standard_normal((130, 256)).astype(np.float32)
