@@ -261,3 +261,44 @@ def test_pages_beyond_4gib():
     qb = synth.attn_queries(300, h, d, seed=127)
     order = [0, 1, 2, 3, 4, 5]
     _check(gpu, ora, order, 1400 - 5 * p, qb, 1 / math.sqrt(d), 6)
+
+
+def test_seeded_config_sweep():
+    """12 seeded caches: 1-6 heads, head_dim 64 or 128, pages of 64, 128 or 256 tokens,
+    1-3 chunks of random lengths (every chunk after the first at least a page) in a
+    shuffled table with spare physical pages.  Pool bytes, means, scales and page->chunk
+    entries and a window read in random page order are bit-exact; the attention over
+    the window (random query count) is within the tolerance."""
+    rng = np.random.default_rng(79)
+    for i in range(12):
+        h, d, p = int(rng.integers(1, 7)), int(rng.choice([64, 128])), int(rng.choice([64, 128, 256]))
+        n_chunks = int(rng.integers(1, 4))
+        lens = [int(rng.integers(1, 3 * p))] + [int(rng.integers(p, 3 * p)) for _ in range(n_chunks - 1)]
+        total = sum(lens)
+        n_pages = -(-total // p)
+        n_phys = n_pages + int(rng.integers(0, 4))
+        table = rng.permutation(n_phys)[:n_pages].astype(np.int32)[None, :]
+        n_q = int(rng.integers(1, 601))
+        print(f"[sweep {i}] heads {h} head_dim {d} page {p} chunks {lens} queries {n_q}", flush=True)
+        gpu, ora = _pair(h, p, n_pages, n_chunks, table, n_phys, d=d)
+        kb, vb = synth.kv_chunk(t=total, h=h, d=d, seed_k=200 + i, seed_v=300 + i, seed_off=400 + i)
+        start = 0
+        for c, n in enumerate(lens):
+            _write(gpu, ora, c, kb[start:start + n], vb[start:start + n], start)
+            start += n
+        torch.cuda.synchronize()
+        for lp in range(n_pages):
+            g = gpu.pool[int(table[0, lp])].cpu().numpy()
+            assert np.array_equal(g, ora.pool[int(table[0, lp])]), (i, lp)
+        for name in ("k_mean", "k_gscale", "v_gscale", "page_chunk"):
+            assert np.array_equal(getattr(gpu, name)[0].cpu().numpy(), getattr(ora, name)[0]), (i, name)
+        order = [int(x) for x in rng.permutation(n_pages)]
+        lp = torch.tensor(order, dtype=torch.int32, device=dev())
+        kh, vh = nv.nvfp4_kv_dequant_blocks(gpu, 0, lp)
+        torch.cuda.synchronize()
+        ko, vo = ora.dequant_pages(0, order)
+        assert np.array_equal(kh.float().cpu().numpy().astype(np.float64), ko), i
+        assert np.array_equal(vh.float().cpu().numpy().astype(np.float64), vo), i
+        window = [x for x in order if x != n_pages - 1] + [n_pages - 1]
+        qb = synth.attn_queries(n_q, h, d, seed=500 + i)
+        _check(gpu, ora, window, total - (n_pages - 1) * p, qb, 1 / math.sqrt(d), n_phys)
