@@ -62,6 +62,29 @@ def test_bf16_several_tiles_two_groups(layout):
     assert same > 0.99
 
 
+def test_seeded_shape_sweep():
+    """16 seeded inputs: rows in [1, 500], cols a multiple of 16 up to 2400 (tiled layout
+    where rows % 128 == 0 and cols % 64 == 0), rows per modulation group from 1 to all,
+    row offsets and magnitudes varied, bf16 or fp32; bytes bit-exact on the kernel's
+    statistics."""
+    rng = np.random.default_rng(80)
+    for i in range(16):
+        rows, cols = int(rng.integers(1, 501)), 16 * int(rng.integers(1, 151))
+        if i % 4 == 0:
+            rows, cols = 128 * int(rng.integers(1, 4)), 64 * int(rng.integers(1, 38))
+        rpg = int(rng.integers(1, rows + 1))
+        x = (rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-8, 9, (rows, 1)))
+             + rng.standard_normal((rows, 1)) * 4).astype(np.float32)
+        shift, scale = synth.adaln_modulation(-(-rows // rpg), cols, seed=600 + i)
+        layout = nv.SCALES_TILED if (rows % 128 == 0 and cols % 64 == 0) else nv.SCALES_ROWMAJOR
+        print(f"[sweep {i}] {rows} x {cols} rows/group {rpg} layout {layout}", flush=True)
+        if rng.integers(2):
+            bits = synth.to_bf16_bits(x)
+            _run(bits, bf16_tensor(bits), shift, scale, rpg, 1e-6, layout)
+        else:
+            _run(x, f32_tensor(x), shift, scale, rpg, 1e-6, layout)
+
+
 def test_fp32_small_groups_tiled():
     # rows_per_group 5 < 29: a lane's eight rows can meet more than two groups
     x = synth.normal_f32((256, 192), 2.0, seed=74) + np.float32(0.5)

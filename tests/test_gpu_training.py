@@ -42,6 +42,26 @@ def test_ragged_tiles_fp32_and_bf16():
     _qt(F.bf16_bits_to_f64(bits), bf16_tensor(bits), nv.SCALES_ROWMAJOR)
 
 
+def test_seeded_shape_sweep():
+    """16 seeded inputs: rows and cols multiples of 16 up to 800 and 704 (tiled layout
+    where cols % 128 == 0 and rows % 64 == 0), column magnitudes over 2^-10 .. 2^10,
+    bf16 or fp32, a quarter with the amax given; bytes bit-exact."""
+    rng = np.random.default_rng(81)
+    for i in range(16):
+        rows, cols = 16 * int(rng.integers(1, 51)), 16 * int(rng.integers(1, 45))
+        if i % 4 == 0:
+            rows, cols = 64 * int(rng.integers(1, 13)), 128 * int(rng.integers(1, 6))
+        x = (rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-10, 11, (1, cols)))).astype(np.float32)
+        layout = nv.SCALES_TILED if (cols % 128 == 0 and rows % 64 == 0) else nv.SCALES_ROWMAJOR
+        amax = float(np.float32(np.max(np.abs(x)) * 1.25)) if i % 4 == 1 else None
+        print(f"[sweep {i}] {rows} x {cols} layout {layout} amax {amax}", flush=True)
+        if rng.integers(2):
+            bits = synth.to_bf16_bits(x)
+            _qt(F.bf16_bits_to_f64(bits), bf16_tensor(bits), layout, amax=amax)
+        else:
+            _qt(x.astype(np.float64), f32_tensor(x), layout, amax=amax)
+
+
 def test_strided_input_and_given_amax():
     x = synth.entry_outliers_f32(256, 128, seed=22, idx_seed=23)
     buf = torch.zeros((256, 160), dtype=torch.float32, device=dev())
