@@ -174,6 +174,27 @@ def test_dequantize_large_random_bytes_both_layouts():
             assert np.array_equal(y, Q.dequantize(q, fmt))
 
 
+def test_dequantize_seeded_shape_sweep():
+    """16 seeded NVFP4 tensors of random bytes: rows in [1, 600], cols a multiple of 16 up
+    to 1600 (tiled where rows % 128 == 0 and cols % 64 == 0), every finite scale byte,
+    s_g over 2^-30 .. 2^30 with random significands; fp32 and bf16 output bit-exact."""
+    rng = np.random.default_rng(82)
+    for i in range(16):
+        r, c = int(rng.integers(1, 601)), 16 * int(rng.integers(1, 101))
+        if i % 4 == 0:
+            r, c = 128 * int(rng.integers(1, 5)), 64 * int(rng.integers(1, 26))
+        packed = rng.integers(0, 256, (r, c // 2)).astype(np.uint8)
+        scales = rng.integers(0, 127, (r, c // 16)).astype(np.uint8)
+        s_g = float(np.float32(rng.uniform(1.0, 2.0) * 2.0 ** int(rng.integers(-30, 31))))
+        q = Q.NVFP4(packed, scales, s_g)
+        layout = nv.SCALES_TILED if (r % 128 == 0 and c % 64 == 0) else nv.SCALES_ROWMAJOR
+        print(f"[sweep {i}] {r} x {c} layout {layout} s_g {s_g!r}", flush=True)
+        t = from_oracle(q, layout)
+        for dt, fmt in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
+            y = nv.nvfp4_dequantize(t, dt).float().cpu().numpy().astype(np.float64)
+            assert np.array_equal(y, Q.dequantize(q, fmt)), (i, fmt)
+
+
 def test_deterministic_bytes():
     d = synth.attn_proj(m=256, k=1024, n=64)
     xd = bf16_tensor(d["x"])
